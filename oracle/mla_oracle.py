@@ -1,0 +1,267 @@
+"""CPU oracle for Multi-head Latent Attention (MLA) decode over a paged latent cache.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call this module.  The HIP library never does, and this module imports
+nothing from it: the two share only the seeded input generator (``synth``), which holds no attention
+arithmetic.
+
+Everything here is plain numpy in float64, written for a reader checking it against the pages:
+
+* "DeepSeek-V2" explainer (aiany.app) -- Step 2 (the attention recipe and the MHA cache bill),
+  Step 5 (eq. 9: one latent note c per token, re-inflated by W^UK and W^UV), Step 6 (absorption:
+  q.k = (W^Q h).(W^UK c), so the key is never built; W^UV folds into the output side), Step 7
+  (decoupled RoPE: a per-head 64-dim q^R and one shared 64-dim rotated k^R, whose score adds to the
+  content score inside the softmax) and Step 8 (576 cached numbers per token per layer).
+* "DeepSeek-V2" paper breakdown (AI360Xpert), "How It Works": only c_t is cached; at generation time
+  it is multiplied by up-projection matrices to rebuild K and V; a separate small RoPE key is kept
+  beside it.  That is the *decompressed* form, and it is the form ``decode_reference`` computes.
+* "DeepSeek (AI)" wiki, "KV cache compression": one key-value vector per (token, layer) instead of a
+  key and a value per head, a cut of (d_K + d_V)/d_KV times the head count.
+
+Layouts (the library's, restated so the oracle stands alone):
+  cache        uint16 (bf16 bits) [num_pages][page_size][d_c + d_R]; a row is [c | k^R]
+  block_table  int32 [B][max_blocks]; token t of sequence b sits in page block_table[b][t // page],
+               slot t % page
+  q            [B][H][d_nope + d_R] = [q_nope | q^R] (q^R and k^R arrive already rotated)
+  W_UK         [H][d_nope][d_c]:  content key of head h is k_h = W_UK[h] @ c
+  W_UV         [H][d_c][d_v]:     value of head h is v_h = c @ W_UV[h]
+  q_abs        [B][H][d_c + d_R] = [W_UK[h]^T q_nope | q^R], the query in latent form
+
+Readings where the pages are silent (each also listed in the design notes):
+  * the softmax scale is an argument (the score formula of Step 7 did not survive extraction);
+  * decode has one query that attends to every cached token of its sequence, position 0 .. len-1,
+    including the row appended this step -- no mask inside that range;
+  * a sequence of length 0 yields o = 0 and lse = -inf;
+  * lse is the natural log of the softmax denominator of the *scaled* scores.
+
+Every function here is pinned by a test in ``tests/test_oracle_*.py`` against the explainer's worked
+2-D example (Step 6), its cache arithmetic (Steps 2 and 8), brute-force loops on tiny shapes, closed
+forms and invariants.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------------------
+# bf16 storage
+# --------------------------------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16/int16) -> float64, exactly (bf16 is the top half of a float32)."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------------------
+# Paged cache bookkeeping (integer, exact)
+# --------------------------------------------------------------------------------------------------
+
+
+def page_and_slot(block_table: np.ndarray, b: int, t, page_size: int):
+    """Physical (page, slot) of logical token t of sequence b."""
+    t = np.asarray(t)
+    return block_table[b, t // page_size], t % page_size
+
+
+def gather_rows(cache: np.ndarray, block_table: np.ndarray, b: int, length: int) -> np.ndarray:
+    """The ``length`` cached rows of sequence b in logical order (raw stored values, no arithmetic)."""
+    page_size = cache.shape[1]
+    pages, slots = page_and_slot(block_table, b, np.arange(length), page_size)
+    if length and (pages < 0).any():
+        raise ValueError("block table has no page for a token inside the sequence")
+    return cache[pages, slots]
+
+
+def append_rows(cache: np.ndarray, block_table: np.ndarray, positions, new_rows) -> np.ndarray:
+    """Return a copy of ``cache`` with new_rows[b] stored at logical position positions[b] of
+    sequence b (each new token's note is written once and never changes: explainer Step 2)."""
+    out = cache.copy()
+    page_size = cache.shape[1]
+    for b, p in enumerate(np.asarray(positions)):
+        page, slot = page_and_slot(block_table, b, int(p), page_size)
+        if page < 0:
+            raise ValueError("block table has no page for the appended position")
+        out[page, slot] = new_rows[b]
+    return out
+
+
+# --------------------------------------------------------------------------------------------------
+# The method in decompressed form (breakdown "How It Works"; explainer Steps 5 and 7)
+# --------------------------------------------------------------------------------------------------
+
+
+def softmax_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float):
+    """Textbook attention for one query (explainer Step 2): score every key, softmax, mix values.
+
+    Returns (out, lse, p).  For zero keys: out = 0, lse = -inf, p empty."""
+    if keys.shape[0] == 0:
+        return np.zeros(values.shape[1]), -math.inf, np.zeros(0)
+    s = scale * (keys @ q)
+    m = s.max()
+    e = np.exp(s - m)
+    z = e.sum()
+    p = e / z
+    return p @ values, m + math.log(z), p
+
+
+def decompress_head(rows: np.ndarray, w_uk_h: np.ndarray, w_uv_h: np.ndarray, d_c: int):
+    """Rebuild one head's content keys and values from the cached notes (explainer Step 5;
+    breakdown "How It Works" step 3): K[t] = W_UK[h] @ c_t, V[t] = c_t @ W_UV[h]."""
+    c = rows[:, :d_c]
+    return c @ w_uk_h.T, c @ w_uv_h
+
+
+def decode_head(q_h: np.ndarray, rows: np.ndarray, w_uk_h: np.ndarray, w_uv_h: np.ndarray,
+                scale: float):
+    """One head, one sequence, decompressed form.
+
+    The full key of token t is [W_UK[h] c_t | k^R_t] and the query is [q_nope | q^R]; their dot
+    product is the content score plus the position score, the two channels adding inside the
+    softmax (explainer Step 7).  k^R is the same for every head (Step 7).  Returns (out, lse, p)."""
+    d_nope, d_c = w_uk_h.shape
+    k_nope, v = decompress_head(rows, w_uk_h, w_uv_h, d_c)
+    keys = np.concatenate([k_nope, rows[:, d_c:]], axis=1)
+    assert keys.shape[1] == q_h.shape[0]
+    return softmax_attention(q_h, keys, v, scale)
+
+
+# --------------------------------------------------------------------------------------------------
+# Plain definitions of the absorbed pieces (explainer Step 6)
+# --------------------------------------------------------------------------------------------------
+
+
+def absorb_query(q_h: np.ndarray, w_uk_h: np.ndarray) -> np.ndarray:
+    """[q_nope | q^R] -> [W_UK[h]^T q_nope | q^R]: the content query moved into latent space, so that
+    q_lat . c_t equals q_nope . (W_UK[h] c_t) without building the key (explainer Step 6)."""
+    d_nope = w_uk_h.shape[0]
+    return np.concatenate([w_uk_h.T @ q_h[:d_nope], q_h[d_nope:]])
+
+
+def latent_attention(q_abs_h: np.ndarray, rows: np.ndarray, d_c: int, scale: float):
+    """Attention of a latent-form query against the cached rows themselves: score = q_abs . row,
+    values = the latent notes c_t.  Returns (o_lat, lse, p)."""
+    return softmax_attention(q_abs_h, rows, rows[:, :d_c], scale)
+
+
+def up_project(o_lat_h: np.ndarray, w_uv_h: np.ndarray) -> np.ndarray:
+    """Per-head value up-projection applied after the weighted sum: o_lat @ W_UV[h]."""
+    return o_lat_h @ w_uv_h
+
+
+def merge_partials(outs, lses):
+    """Combine attention over disjoint token sets: each part carries its normalised output and the
+    log of its softmax denominator.  L = log sum_s e^{lse_s}; o = sum_s e^{lse_s - L} o_s."""
+    lses = np.asarray(lses, dtype=np.float64)
+    outs = np.asarray(outs, dtype=np.float64)
+    if np.all(np.isneginf(lses)):
+        return np.zeros(outs.shape[1:]), -math.inf
+    m = lses.max()
+    w = np.exp(lses - m)
+    big_l = m + math.log(w.sum())
+    return np.tensordot(np.exp(lses - big_l), outs, axes=1), big_l
+
+
+# --------------------------------------------------------------------------------------------------
+# Batched drivers
+# --------------------------------------------------------------------------------------------------
+
+
+def _sel(n, subset):
+    return range(n) if subset is None else list(subset)
+
+
+def absorb_batch(q, w_uk, batch=None, heads=None) -> np.ndarray:
+    """q_abs[b][h] for the selected (b, h); other entries NaN.  Inputs are bf16 bits or floats."""
+    q = _f64(q)
+    w_uk = _f64(w_uk)
+    B, H, _ = q.shape
+    d_c = w_uk.shape[2]
+    out = np.full((B, H, d_c + q.shape[2] - w_uk.shape[1]), np.nan)
+    for b in _sel(B, batch):
+        for h in _sel(H, heads):
+            out[b, h] = absorb_query(q[b, h], w_uk[h])
+    return out
+
+
+def out_proj_batch(o_lat, w_uv, batch=None, heads=None) -> np.ndarray:
+    o_lat = _f64(o_lat)
+    w_uv = _f64(w_uv)
+    B, H, _ = o_lat.shape
+    out = np.full((B, H, w_uv.shape[2]), np.nan)
+    for b in _sel(B, batch):
+        for h in _sel(H, heads):
+            out[b, h] = up_project(o_lat[b, h], w_uv[h])
+    return out
+
+
+def latent_decode_batch(q_abs, cache, block_table, seq_lens, scale, d_c=512, batch=None,
+                        heads=None):
+    """Reference for the latent-space decode step: o_lat [B][H][d_c] and lse [B][H]."""
+    q_abs = _f64(q_abs)
+    B, H, _ = q_abs.shape
+    o = np.full((B, H, d_c), np.nan)
+    lse = np.full((B, H), np.nan)
+    for b in _sel(B, batch):
+        rows = _f64(gather_rows(cache, block_table, b, int(seq_lens[b])))
+        for h in _sel(H, heads):
+            o[b, h], lse[b, h], _ = latent_attention(q_abs[b, h], rows, d_c, scale)
+    return o, lse
+
+
+def decode_reference(q, cache, block_table, seq_lens, w_uk, w_uv, scale, batch=None, heads=None):
+    """End-to-end reference, decompressed form: out [B][H][d_v] and lse [B][H]."""
+    q = _f64(q)
+    w_uk = _f64(w_uk)
+    w_uv = _f64(w_uv)
+    B, H, _ = q.shape
+    out = np.full((B, H, w_uv.shape[2]), np.nan)
+    lse = np.full((B, H), np.nan)
+    for b in _sel(B, batch):
+        rows = _f64(gather_rows(cache, block_table, b, int(seq_lens[b])))
+        for h in _sel(H, heads):
+            out[b, h], lse[b, h], _ = decode_head(q[b, h], rows, w_uk[h], w_uv[h], scale)
+    return out, lse
+
+
+def _f64(x) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype in (np.uint16, np.int16):
+        return bf16_to_f64(x)
+    return x.astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------------------
+# Cache arithmetic (explainer Steps 2 and 8; wiki "KV cache compression")
+# --------------------------------------------------------------------------------------------------
+
+
+def mha_numbers_per_token(heads: int, head_dim: int, layers: int) -> int:
+    """Standard multi-head caching: one key and one value per head per layer (explainer Step 2)."""
+    return 2 * heads * head_dim * layers
+
+
+def mla_numbers_per_token(d_c: int, d_r: int, layers: int) -> int:
+    """MLA caching: the latent note plus the shared RoPE key, per layer (explainer Step 8)."""
+    return (d_c + d_r) * layers
+
+
+def cache_bytes(numbers: int, bits_per_number: float) -> float:
+    return numbers * bits_per_number / 8.0
+
+
+def gqa_equivalent_groups(d_c: int, d_r: int, head_dim: int) -> float:
+    """GQA with g groups caches 2 * g * head_dim numbers per layer; the g that matches MLA's row."""
+    return (d_c + d_r) / (2.0 * head_dim)
+
+
+def gqa_numbers_per_token(groups: int, head_dim: int, layers: int) -> int:
+    """Grouped-query caching: one key and one value per group per layer (explainer Step 4)."""
+    return 2 * groups * head_dim * layers
+
+
+def wiki_reduction_factor(d_k: int, d_v: int, d_kv: int, heads: int) -> float:
+    """(d_K + d_V) / d_KV x heads (wiki "KV cache compression")."""
+    return (d_k + d_v) / d_kv * heads

@@ -1,0 +1,339 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself.
+
+* the explainer's 2-D absorption example with its printed numbers (golden fixture);
+* the explainer's and the wiki's cache arithmetic (golden fixture);
+* brute force with explicit Python loops on tiny shapes, non-square so a transposed operand fails;
+* closed forms and special cases (one token, zero query, identical rows, the needle);
+* invariants (absorbed == decompressed, split-and-merge == single pass, softmax sums to one).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------------------------------
+# The explainer's worked example (Step 6)
+# --------------------------------------------------------------------------------------------------
+
+def test_toy_absorption_example():
+    g = _load("toy_absorption.json")
+    w_q = np.array(g["W_Q"], float)
+    w_uk = np.array(g["W_UK"], float)
+    h = np.array(g["h"], float)
+    c = np.array(g["c"], float)
+    q = w_q @ h
+    assert q.tolist() == g["q"]
+    # slow path: rebuild the key from the note, then score
+    row = c[None, :]                        # one cached token, no RoPE part
+    k_nope, _ = O.decompress_head(row, w_uk, np.eye(2), d_c=2)
+    assert k_nope[0].tolist() == g["k"]
+    assert float(q @ k_nope[0]) == g["score"]
+    # absorbed path: move the query into latent space, score the note directly
+    q_lat = O.absorb_query(q, w_uk)
+    assert float(q_lat @ c) == g["score"]
+    # the merged matrix M = W_Q^T W_UK, built column by column with the oracle's absorption
+    m = np.stack([O.absorb_query(w_q @ e, w_uk) for e in np.eye(2)])
+    assert m.tolist() == g["M"]
+    assert (m @ c).tolist() == g["Mc"]
+    assert float(h @ (m @ c)) == g["score"]
+
+
+def test_toy_example_through_decode_head():
+    """With one token, softmax weight is 1 and lse equals the (scaled) score 13."""
+    g = _load("toy_absorption.json")
+    q = np.array(g["q"], float)
+    w_uk = np.array(g["W_UK"], float)
+    rows = np.array([g["c"]], float)          # d_c = 2, d_R = 0
+    out, lse, p = O.decode_head(q, rows, w_uk, np.eye(2), scale=1.0)
+    assert p.tolist() == [1.0]
+    assert lse == g["score"]
+    o_lat, lse2, _ = O.latent_attention(O.absorb_query(q, w_uk), rows, 2, 1.0)
+    assert lse2 == g["score"]
+    assert o_lat.tolist() == g["c"]
+
+
+# --------------------------------------------------------------------------------------------------
+# Cache arithmetic (explainer Steps 2, 4, 5, 8; wiki)
+# --------------------------------------------------------------------------------------------------
+
+def test_cache_arithmetic_closed_forms():
+    g = _load("cache_arithmetic.json")
+    s = g["shapes"]
+    mha = O.mha_numbers_per_token(s["heads"], s["head_dim"], s["layers"])
+    assert mha == 1_966_080
+    assert O.mha_numbers_per_token(s["heads"], s["head_dim"], 1) == g["step5"]["numbers_of_keys_and_values_per_layer"]
+    assert round(O.cache_bytes(mha, 16) / 1e6, 2) == g["step2"]["mb_per_token_bf16"]
+    report = O.cache_bytes(mha, 16) * s["report_tokens"] / 1e9
+    assert abs(report - g["step2"]["gb_per_report_approx"]) < 1.0
+    assert report < g["step2"]["node_gb"]
+    # Step 4: grouped and multi-query caching
+    assert mha // O.gqa_numbers_per_token(g["step4"]["gqa_groups"], s["head_dim"], s["layers"]) == g["step4"]["gqa_cut"]
+    assert mha // O.gqa_numbers_per_token(1, s["head_dim"], s["layers"]) == g["step4"]["mqa_cut"]
+    # Step 8: the MLA row
+    assert O.mla_numbers_per_token(s["d_c"], s["d_r"], 1) == g["step8"]["numbers_per_token_per_layer"]
+    mla = O.mla_numbers_per_token(s["d_c"], s["d_r"], s["layers"])
+    assert mla == 34_560
+    assert round(mha / mla, 1) == g["step8"]["factor"]
+    assert round(O.cache_bytes(mla, 16) * s["report_tokens"] / 1e9, 1) == g["step8"]["gb_per_report_approx"]
+    assert O.gqa_equivalent_groups(s["d_c"], s["d_r"], s["head_dim"]) == g["step8"]["gqa_equivalent_groups"]
+    assert round(100 * (1 - mla / mha), 1) == g["step8"]["same_precision_reduction_pct"]
+    # the 93.3% audit: the dense 67B model (95 layers, GQA with Step 4's 8 groups) at 2 bytes per
+    # number against V2 at about 6 bits per number
+    d67 = O.gqa_numbers_per_token(g["step4"]["gqa_groups"], s["head_dim"], g["step8"]["dense67b_layers"])
+    assert abs(d67 - g["step8"]["dense67b_numbers_approx"]) < 1000
+    d67_kb = O.cache_bytes(d67, 16) / 1e3
+    assert round(d67_kb) == g["step8"]["dense67b_kb_approx"]
+    v2_kb = O.cache_bytes(mla, g["step8"]["v2_bits_per_number"]) / 1e3
+    assert round(v2_kb) == g["step8"]["v2_kb_approx"]
+    assert round(100 * v2_kb / d67_kb, 1) == g["step8"]["ratio_pct_approx"]
+    assert round(100 * (1 - v2_kb / d67_kb), 1) == g["step8"]["headline_reduction_pct"]
+    # wiki: (d_K + d_V) / d_KV x heads, with the MLA row as d_KV
+    f = O.wiki_reduction_factor(s["head_dim"], s["head_dim"], s["d_c"] + s["d_r"], s["heads"])
+    assert round(f, 1) == g["wiki"]["factor_approx"] == round(mha / mla, 1)
+
+
+# --------------------------------------------------------------------------------------------------
+# Brute force on tiny shapes
+# --------------------------------------------------------------------------------------------------
+
+def _tiny(seed, lens, H=2, d_c=8, d_r=4, d_nope=4, d_v=3, page=2):
+    rng = np.random.default_rng(seed)
+    blocks = [(n + page - 1) // page for n in lens]
+    total = sum(blocks)
+    perm = rng.permutation(total)
+    mb = max(max(blocks), 1)
+    bt = np.full((len(lens), mb), -1, np.int32)
+    k = 0
+    for b, nb in enumerate(blocks):
+        bt[b, :nb] = perm[k:k + nb]
+        k += nb
+    cache = rng.normal(size=(total, page, d_c + d_r))
+    q = rng.normal(size=(len(lens), H, d_nope + d_r))
+    w_uk = rng.normal(size=(H, d_nope, d_c)) / math.sqrt(d_c)
+    w_uv = rng.normal(size=(H, d_c, d_v)) / math.sqrt(d_c)
+    return cache, bt, q, w_uk, w_uv
+
+
+def _brute(cache, bt, q, w_uk, w_uv, lens, scale):
+    """Explicit loops straight from the definitions: rebuild each head's key and value from the
+    note, add the RoPE score, softmax, mix."""
+    page = cache.shape[1]
+    B, H, _ = q.shape
+    d_nope, d_c = w_uk.shape[1], w_uk.shape[2]
+    d_v = w_uv.shape[2]
+    out = np.zeros((B, H, d_v))
+    lse = np.zeros((B, H))
+    for b in range(B):
+        for h in range(H):
+            scores = []
+            values = []
+            for t in range(lens[b]):
+                row = cache[bt[b][t // page]][t % page]
+                c = row[:d_c]
+                k_r = row[d_c:]
+                s = 0.0
+                for i in range(d_nope):
+                    k_i = 0.0
+                    for j in range(d_c):
+                        k_i += w_uk[h][i][j] * c[j]
+                    s += q[b][h][i] * k_i
+                for i in range(len(k_r)):
+                    s += q[b][h][d_nope + i] * k_r[i]
+                scores.append(scale * s)
+                v = [sum(c[j] * w_uv[h][j][d] for j in range(d_c)) for d in range(d_v)]
+                values.append(v)
+            m = max(scores)
+            z = sum(math.exp(x - m) for x in scores)
+            for t in range(lens[b]):
+                w = math.exp(scores[t] - m) / z
+                for d in range(d_v):
+                    out[b][h][d] += w * values[t][d]
+            lse[b][h] = m + math.log(z)
+    return out, lse
+
+
+@pytest.mark.parametrize("lens", [[1], [2], [3, 5], [5, 1, 2]])
+def test_decode_reference_vs_brute_force(lens):
+    cache, bt, q, w_uk, w_uv = _tiny(7 + len(lens), lens)
+    scale = 0.37
+    out, lse = O.decode_reference(q, cache.astype(np.float64), bt, lens, w_uk, w_uv, scale)
+    bo, bl = _brute(cache, bt, q, w_uk, w_uv, lens, scale)
+    np.testing.assert_allclose(out, bo, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, bl, rtol=1e-12, atol=1e-13)
+
+
+def test_latent_decode_vs_brute_force():
+    lens = [3, 5]
+    cache, bt, q, w_uk, w_uv = _tiny(3, lens)
+    d_c = w_uk.shape[2]
+    q_abs = O.absorb_batch(q, w_uk)
+    o_lat, lse = O.latent_decode_batch(q_abs, cache, bt, lens, 0.5, d_c=d_c)
+    page = cache.shape[1]
+    for b in range(len(lens)):
+        for h in range(q.shape[1]):
+            s = []
+            for t in range(lens[b]):
+                row = cache[bt[b][t // page]][t % page]
+                s.append(0.5 * sum(q_abs[b][h][i] * row[i] for i in range(len(row))))
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            z = sum(w)
+            ref = [sum(w[t] / z * cache[bt[b][t // page]][t % page][j] for t in range(lens[b]))
+                   for j in range(d_c)]
+            np.testing.assert_allclose(o_lat[b, h], ref, rtol=1e-12, atol=1e-14)
+            assert abs(lse[b, h] - (m + math.log(z))) < 1e-12
+
+
+# --------------------------------------------------------------------------------------------------
+# Invariants and special cases at the real widths (d_c = 512, d_R = 64, d_nope = d_v = 128)
+# --------------------------------------------------------------------------------------------------
+
+def _real(seed, T, H=3):
+    rng = np.random.default_rng(seed)
+    rows = rng.normal(size=(T, 576))
+    q = rng.normal(size=(H, 192))
+    w_uk = rng.normal(size=(H, 128, 512)) / math.sqrt(512)
+    w_uv = rng.normal(size=(H, 512, 128)) / math.sqrt(512)
+    return rows, q, w_uk, w_uv
+
+
+def test_absorbed_equals_decompressed():
+    rows, q, w_uk, w_uv = _real(1, 300)
+    scale = 1 / math.sqrt(192)
+    for h in range(q.shape[0]):
+        out, lse, p = O.decode_head(q[h], rows, w_uk[h], w_uv[h], scale)
+        q_abs = O.absorb_query(q[h], w_uk[h])
+        o_lat, lse2, p2 = O.latent_attention(q_abs, rows, 512, scale)
+        out2 = O.up_project(o_lat, w_uv[h])
+        np.testing.assert_allclose(out2, out, rtol=1e-11, atol=1e-13)
+        assert abs(lse - lse2) < 1e-11
+        np.testing.assert_allclose(p2, p, rtol=1e-11, atol=1e-15)
+        assert abs(p.sum() - 1) < 1e-12
+
+
+def test_channels_add_inside_softmax():
+    """Zeroing q^R leaves the content-only score; zeroing q_nope leaves the RoPE-only score."""
+    rows, q, w_uk, w_uv = _real(2, 50, H=1)
+    s_full = O.decode_head(q[0], rows, w_uk[0], w_uv[0], 1.0)[1]
+    q_c = q[0].copy(); q_c[128:] = 0
+    q_r = q[0].copy(); q_r[:128] = 0
+    k_nope = rows[:, :512] @ w_uk[0].T
+    s_c = k_nope @ q[0][:128]
+    s_r = rows[:, 512:] @ q[0][128:]
+    assert abs(O.decode_head(q_c, rows, w_uk[0], w_uv[0], 1.0)[1] - np.log(np.exp(s_c).sum())) < 1e-10
+    assert abs(O.decode_head(q_r, rows, w_uk[0], w_uv[0], 1.0)[1] - np.log(np.exp(s_r).sum())) < 1e-10
+    assert abs(s_full - np.log(np.exp(s_c + s_r).sum())) < 1e-10
+
+
+def test_single_token_gives_its_value():
+    rows, q, w_uk, w_uv = _real(3, 1)
+    out, lse, p = O.decode_head(q[0], rows, w_uk[0], w_uv[0], 0.1)
+    assert p.tolist() == [1.0]
+    np.testing.assert_array_equal(out, rows[0, :512] @ w_uv[0])
+
+
+def test_zero_query_is_uniform_mean():
+    rows, _, _, _ = _real(4, 37)
+    o_lat, lse, p = O.latent_attention(np.zeros(576), rows, 512, 1.0)
+    np.testing.assert_allclose(p, np.full(37, 1 / 37), rtol=1e-14)
+    np.testing.assert_allclose(o_lat, rows[:, :512].mean(axis=0), rtol=1e-12, atol=1e-14)
+    assert abs(lse - math.log(37)) < 1e-14
+
+
+def test_identical_rows_give_that_row():
+    rows, q, w_uk, _ = _real(5, 1)
+    rep = np.repeat(rows, 9, axis=0)
+    q_abs = O.absorb_query(q[0], w_uk[0])
+    o_lat, _, _ = O.latent_attention(q_abs, rep, 512, 0.3)
+    np.testing.assert_allclose(o_lat, rows[0, :512], rtol=1e-14, atol=1e-15)
+
+
+def test_empty_sequence():
+    o_lat, lse, p = O.latent_attention(np.ones(576), np.zeros((0, 576)), 512, 1.0)
+    assert lse == -math.inf and not o_lat.any() and p.size == 0
+
+
+@pytest.mark.parametrize("cuts", [[0, 200], [0, 1, 200], [0, 64, 65, 128, 200], [0, 7, 100, 199, 200]])
+def test_split_and_merge_equals_single_pass(cuts):
+    rows, q, w_uk, _ = _real(6, 200, H=1)
+    q_abs = O.absorb_query(q[0], w_uk[0])
+    o_ref, l_ref, _ = O.latent_attention(q_abs, rows, 512, 1 / math.sqrt(192))
+    parts = [O.latent_attention(q_abs, rows[a:b], 512, 1 / math.sqrt(192)) for a, b in zip(cuts, cuts[1:])]
+    o, l = O.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-14)
+    assert abs(l - l_ref) < 1e-12
+    # an empty part (lse = -inf) changes nothing
+    o2, l2 = O.merge_partials([p[0] for p in parts] + [np.zeros(512)], [p[1] for p in parts] + [-math.inf])
+    np.testing.assert_allclose(o2, o, rtol=0, atol=0)
+    assert l2 == l
+
+
+def test_needle_selects_one_row_exactly():
+    """A RoPE-only query that matches one token's k^R and opposes every other makes the softmax a
+    one-hot: o_lat equals that token's note exactly."""
+    rng = np.random.default_rng(9)
+    rows = rng.normal(size=(130, 576))
+    rows[:, 512] = -1.0
+    star = 77
+    rows[star, 512] = 1.0
+    q_abs = np.zeros(576)
+    q_abs[512] = 1000.0
+    o_lat, lse, p = O.latent_attention(q_abs, rows, 512, 1 / math.sqrt(192))
+    np.testing.assert_array_equal(o_lat, rows[star, :512])
+    assert p[star] == 1.0
+
+
+# --------------------------------------------------------------------------------------------------
+# Paged bookkeeping
+# --------------------------------------------------------------------------------------------------
+
+def test_gather_and_append_through_a_shuffled_table():
+    page = 4
+    lens = [5, 8, 1]
+    rng = np.random.default_rng(11)
+    blocks = [(n + 1 + page - 1) // page for n in lens]     # room for one append each
+    perm = rng.permutation(sum(blocks))
+    bt = np.full((3, max(blocks)), -1, np.int32)
+    k = 0
+    for b, nb in enumerate(blocks):
+        bt[b, :nb] = perm[k:k + nb]
+        k += nb
+    # fill each logical token with a code that names it: (b, t) -> 1000 b + t
+    cache = np.zeros((sum(blocks), page, 3), np.uint16)
+    for b, n in enumerate(lens):
+        for t in range(n):
+            cache[bt[b][t // page], t % page] = [b, t, 1000 * b + t]
+    for b, n in enumerate(lens):
+        rows = O.gather_rows(cache, bt, b, n)
+        assert [tuple(r) for r in rows] == [(b, t, 1000 * b + t) for t in range(n)]
+    new = np.array([[9, 9, b] for b in range(3)], np.uint16)
+    after = O.append_rows(cache, bt, lens, new)
+    for b, n in enumerate(lens):
+        rows = O.gather_rows(after, bt, b, n + 1)
+        assert tuple(rows[-1]) == (9, 9, b)
+        assert [tuple(r) for r in rows[:-1]] == [(b, t, 1000 * b + t) for t in range(n)]
+    changed = np.argwhere((after != cache).any(axis=2))
+    assert len(changed) == 3
+    with pytest.raises(ValueError):
+        O.gather_rows(cache, np.full((1, 1), -1, np.int32), 0, 1)
+
+
+def test_bf16_widening_is_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x7F7F, 0x0001], np.uint16)
+    vals = O.bf16_to_f64(bits)
+    assert vals[0] == 1.0 and vals[1] == -1.0 and vals[3] == 0.0
+    assert vals[2] == 3.140625
+    assert vals[5] == float(np.float32(3.3895313892515355e38))
+    assert vals[6] == 2.0 ** -133
