@@ -1,0 +1,129 @@
+"""ctypes binding over libmla.so: the C entry points under the same names, taking torch tensors.
+
+Argument marshalling only -- every step of the decode path runs in the HIP kernels of libmla.so.
+PyTorch supplies device memory and the current stream.  If the library is missing this module raises
+at import: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_BF16, MLA_F32 = 0, 1
+STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
+          -4: "MLA_ERR_WORKSPACE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_BLOCK_TABLE",
+          -7: "MLA_ERR_HIP"}
+EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", "mla_cache_append",
+           "mla_absorb_q", "mla_decode", "mla_out_proj")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run head_latent_attention_17_amd.build.build()")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+lib.mla_status_string.restype = ctypes.c_char_p
+lib.mla_status_string.argtypes = [_i]
+lib.mla_abi_version.restype = _i
+lib.mla_abi_version.argtypes = []
+lib.mla_decode_workspace_size.restype = _sz
+lib.mla_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+lib.mla_cache_append.restype = _i
+lib.mla_cache_append.argtypes = [_p, _i, _i, _p, _i, _p, _p, _p, _i, _i, _p]
+lib.mla_absorb_q.restype = _i
+lib.mla_absorb_q.argtypes = [_p, _p, _p, _i, _i, _i, _p]
+lib.mla_decode.restype = _i
+lib.mla_decode.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _p, _sz, _i, _i, _p]
+lib.mla_out_proj.restype = _i
+lib.mla_out_proj.argtypes = [_p, _p, _p, _i, _i, _i, _p]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib.mla_status_string(status).decode()}")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MLAError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_of(t: torch.Tensor) -> int:
+    if t.dtype in (torch.bfloat16, torch.int16):
+        return MLA_BF16
+    if t.dtype == torch.float32:
+        return MLA_F32
+    raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("libmla takes contiguous device tensors")
+
+
+def mla_status_string(status: int) -> str:
+    return lib.mla_status_string(status).decode()
+
+
+def mla_abi_version() -> int:
+    return lib.mla_abi_version()
+
+
+def mla_decode_workspace_size(batch: int, num_heads: int, max_blocks_per_seq: int,
+                              num_splits: int = 0, dtype: int = MLA_BF16) -> int:
+    return int(lib.mla_decode_workspace_size(batch, num_heads, max_blocks_per_seq, num_splits, dtype))
+
+
+def mla_cache_append(kv_cache, block_table, positions, c_new, kpe_new, stream=None):
+    """kv_cache bf16 [pages][64][576] (in place); block_table int32 [B][max_blocks];
+    positions int32 [B]; c_new [B][512], kpe_new [B][64] (bf16, or fp32 for the debug mode)."""
+    _dev(kv_cache, block_table, positions, c_new, kpe_new)
+    _check(lib.mla_cache_append(_ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1],
+                                _ptr(block_table), block_table.shape[1], _ptr(positions),
+                                _ptr(c_new), _ptr(kpe_new), positions.shape[0], _dtype_of(c_new),
+                                _stream(stream)), "mla_cache_append")
+
+
+def mla_absorb_q(q, w_uk, q_abs, stream=None):
+    """q [B][H][192] -> q_abs [B][H][576]; w_uk [H][128][512]."""
+    _dev(q, w_uk, q_abs)
+    _check(lib.mla_absorb_q(_ptr(q), _ptr(w_uk), _ptr(q_abs), q.shape[0], q.shape[1], _dtype_of(q),
+                            _stream(stream)), "mla_absorb_q")
+
+
+def mla_decode(q_abs, kv_cache, block_table, seq_lens, softmax_scale, o_lat, lse=None,
+               workspace=None, num_splits=0, stream=None):
+    """q_abs [B][H][576]; kv_cache bf16 [pages][64][576]; block_table int32 [B][max_blocks];
+    seq_lens int32 [B] -> o_lat [B][H][512] and, if given, lse fp32 [B][H].
+    workspace: a byte tensor of at least mla_decode_workspace_size(...) bytes."""
+    _dev(q_abs, kv_cache, block_table, seq_lens, o_lat, lse, workspace)
+    B, H = q_abs.shape[0], q_abs.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.mla_decode(_ptr(q_abs), _ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1],
+                          _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, H,
+                          float(softmax_scale), _ptr(o_lat), _ptr(lse), _ptr(workspace), ws_bytes,
+                          int(num_splits), _dtype_of(q_abs), _stream(stream)), "mla_decode")
+
+
+def mla_out_proj(o_lat, w_uv, out, stream=None):
+    """o_lat [B][H][512] -> out [B][H][128]; w_uv [H][512][128]."""
+    _dev(o_lat, w_uv, out)
+    _check(lib.mla_out_proj(_ptr(o_lat), _ptr(w_uv), _ptr(out), o_lat.shape[0], o_lat.shape[1],
+                            _dtype_of(o_lat), _stream(stream)), "mla_out_proj")

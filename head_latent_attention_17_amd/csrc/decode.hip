@@ -1,0 +1,209 @@
+// Latent-space decode attention: the vector-ALU kernel (fp32 debug mode and any head count) and
+// the log-sum-exp merge of page ranges that split a sequence.
+//
+// Per sequence b and head h (DeepSeek-V2 explainer, Steps 6-8): every cached row [c_t | k^R_t]
+// is scored by one 576-long dot product with the latent-form query [W_UK^T q_nope | q^R] -- the
+// content score and the RoPE score add inside the softmax -- and the softmax weights average the
+// notes c_t.  The running softmax is kept in base 2: s' = s * scale * log2(e).
+#include "mla_device.h"
+
+namespace mla {
+
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s);
+bool mfma_supported(const DecodeParams& p);
+
+namespace {
+
+constexpr int kTile = 32;             // tokens per LDS tile
+constexpr int kRowDw = kRow / 2 + 1;  // 289 dwords per LDS row: consecutive rows start on different banks
+constexpr int kHG = 16;               // heads per workgroup
+constexpr int kQStride = kRow + 2;    // fp32 query rows, padded
+
+template <typename QT, typename OT>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
+  __shared__ float q_s[kHG][kQStride];
+  __shared__ uint32_t kv_s[kTile][kRowDw];
+  __shared__ float s_s[kHG][kTile + 1];
+  __shared__ float alpha_s[kHG];
+  __shared__ float stat_s[kHG][2];
+
+  const int tid = threadIdx.x;
+  const int w = blockIdx.x;
+  const int h0 = blockIdx.y * kHG;
+  const int hh = tid >> 4;     // head within the group
+  const int j16 = tid & 15;    // token lane for scores, dword lane for the weighted sum
+  const QT* q_abs = static_cast<const QT*>(p.q_abs);
+
+  SegmentWalker walk;
+  walk.init(p.seq_lens, p.batch, p.num_units, w);
+  Segment seg;
+  while (walk.next(seg)) {
+    const int b = seg.b;
+    __syncthreads();
+    for (int i = tid; i < kHG * kRow; i += 256) {
+      const int h = i / kRow, k = i % kRow;
+      q_s[h][k] = Elem<QT>::load(q_abs, ((size_t)b * p.heads + h0 + h) * kRow + k);
+    }
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;  // meaningful in threads tid < kHG (head tid)
+
+    const int t_begin = seg.page0 * kPage;
+    const int t_end = min(seg.page1 * kPage, seg.len);
+    const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
+    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+      const int nt = min(kTile, t_end - t0);
+      __syncthreads();
+      // Stage the tile.  Rows past the end re-read the last valid token (finite, masked below),
+      // so no slot beyond the sequence and no unused block-table entry is ever touched.
+      for (int i = tid; i < kTile * (kRow / 8); i += 256) {
+        const int r = i / (kRow / 8), c = i % (kRow / 8);
+        const int t = t0 + min(r, nt - 1);
+        const int page = bt[t / kPage];
+        const uint4 v = reinterpret_cast<const uint4*>(p.cache + ((size_t)page * kPage + (t % kPage)) * kRow)[c];
+        uint32_t* dst = &kv_s[r][c * 4];
+        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+      }
+      __syncthreads();
+      {
+        float s0 = 0.f, s1 = 0.f;
+        const uint32_t* r0 = kv_s[j16];
+        const uint32_t* r1 = kv_s[j16 + 16];
+        const float* qh = q_s[hh];
+#pragma unroll 8
+        for (int k2 = 0; k2 < kRow / 2; ++k2) {
+          const float qa = qh[2 * k2], qb = qh[2 * k2 + 1];
+          const uint32_t a = r0[k2], c = r1[k2];
+          s0 = fmaf(qa, bf16_lo(a), s0);
+          s0 = fmaf(qb, bf16_hi(a), s0);
+          s1 = fmaf(qa, bf16_lo(c), s1);
+          s1 = fmaf(qb, bf16_hi(c), s1);
+        }
+        s_s[hh][j16] = (j16 < nt) ? s0 * p.scale_log2 : -INFINITY;
+        s_s[hh][j16 + 16] = (j16 + 16 < nt) ? s1 * p.scale_log2 : -INFINITY;
+      }
+      __syncthreads();
+      if (tid < kHG) {
+        float mx = -INFINITY;
+        for (int t = 0; t < kTile; ++t) mx = fmaxf(mx, s_s[tid][t]);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f(m_run - m_new);
+        float sum = 0.f;
+        for (int t = 0; t < kTile; ++t) {
+          const float e = exp2f(s_s[tid][t] - m_new);
+          s_s[tid][t] = e;
+          sum += e;
+        }
+        l_run = l_run * alpha + sum;
+        m_run = m_new;
+        alpha_s[tid] = alpha;
+      }
+      __syncthreads();
+      const float alpha = alpha_s[hh];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+      for (int t = 0; t < kTile; ++t) {
+        const float pt = s_s[hh][t];
+        const uint32_t* rv = kv_s[t];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {  // latent dims 32 j + 2 j16 + {0, 1}
+          const uint32_t v = rv[j * 16 + j16];
+          acc[2 * j] = fmaf(pt, bf16_lo(v), acc[2 * j]);
+          acc[2 * j + 1] = fmaf(pt, bf16_hi(v), acc[2 * j + 1]);
+        }
+      }
+    }
+    if (tid < kHG) {
+      stat_s[tid][0] = m_run;
+      stat_s[tid][1] = l_run;
+    }
+    __syncthreads();
+    // Un-normalised partial sum plus (reference max, softmax sum); the merge kernel finishes it.
+    const size_t part = ((size_t)w + b) * p.heads + h0 + hh;
+    float* o = p.ws_o + part * kDc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      *reinterpret_cast<float2*>(o + 32 * j + 2 * j16) = make_float2(acc[2 * j], acc[2 * j + 1]);
+    if (j16 == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(stat_s[hh][0], stat_s[hh][1]);
+  }
+}
+
+// Finishes every sequence: combines its pieces (one per work unit it touches, stored at slot
+// unit + sequence), divides by the softmax sum and writes o_lat and lse.
+//   M = max_s m_s;  w_s = 2^(m_s - M);  o = sum_s w_s o_s / sum_s w_s l_s;  lse = ln2 (M + log2 sum_s w_s l_s)
+// One workgroup per (sequence, 4 heads); 64 lanes per head, 8 latent dims per lane.
+template <typename OT>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
+  const int b = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int len = p.seq_lens[b];
+  const long long np = pages_of(len);
+  OT* o = static_cast<OT*>(p.o_lat);
+  const size_t ob = ((size_t)b * p.heads + h) * kDc + lane * 8;
+  if (np == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Elem<OT>::store(o, ob + i, 0.f);
+    if (p.lse && lane == 0) p.lse[(size_t)b * p.heads + h] = -INFINITY;
+    return;
+  }
+  const long long P = total_pages(p.seq_lens, p.batch);
+  const long long before = pages_before(p.seq_lens, b);
+  const int W = p.num_units;
+  const int wf = unit_of_page(P, W, before);
+  const int wl = unit_of_page(P, W, before + np - 1);
+
+  float mx = -INFINITY;
+  for (int w = wf; w <= wl; ++w) {
+    if (unit_start(P, W, w) == unit_start(P, W, w + 1)) continue;
+    mx = fmaxf(mx, p.ws_ml[2 * (((size_t)w + b) * p.heads + h)]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  for (int w = wf; w <= wl; ++w) {
+    if (unit_start(P, W, w) == unit_start(P, W, w + 1)) continue;
+    const size_t part = ((size_t)w + b) * p.heads + h;
+    const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + 2 * part);
+    const float wgt = exp2f(ml.x - mx);
+    sum = fmaf(wgt, ml.y, sum);
+    const float4* src = reinterpret_cast<const float4*>(p.ws_o + part * kDc + lane * 8);
+    const float4 a = src[0], c = src[1];
+    acc[0] = fmaf(wgt, a.x, acc[0]); acc[1] = fmaf(wgt, a.y, acc[1]);
+    acc[2] = fmaf(wgt, a.z, acc[2]); acc[3] = fmaf(wgt, a.w, acc[3]);
+    acc[4] = fmaf(wgt, c.x, acc[4]); acc[5] = fmaf(wgt, c.y, acc[5]);
+    acc[6] = fmaf(wgt, c.z, acc[6]); acc[7] = fmaf(wgt, c.w, acc[7]);
+  }
+  const float inv = 1.f / sum;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) Elem<OT>::store(o, ob + i, acc[i] * inv);
+  if (p.lse && lane == 0) p.lse[(size_t)b * p.heads + h] = (mx + log2f(sum)) * 0.69314718055994531f;
+}
+
+template <typename T>
+hipError_t launch_valu(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((decode_valu_kernel<T, T>), dim3(p.num_units, p.heads / kHG), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(merge_kernel<T>, dim3(p.batch, p.heads / 4), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, bool f32, hipStream_t s) {
+  hipError_t e;
+  if (f32) {
+    e = launch_valu<float>(p, s);
+    if (e == hipSuccess) e = launch_merge<float>(p, s);
+  } else {
+    e = mfma_supported(p) ? launch_decode_mfma(p, s) : launch_valu<uint16_t>(p, s);
+    if (e == hipSuccess) e = launch_merge<uint16_t>(p, s);
+  }
+  return e;
+}
+
+}  // namespace mla

@@ -1,0 +1,132 @@
+// C ABI of libmla: host-side validation, workspace sizing and dispatch.  No device code here;
+// every check runs before any HIP call, so argument errors are reported without a GPU.
+#include "../../include/mla.h"
+
+#include <math.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+int auto_units(int batch, int heads, int max_blocks) {
+  // Enough page ranges to give every compute unit work, but never more ranges than pages.
+  const long long pages_bound = (long long)batch * (long long)max_blocks;
+  long long units = (heads >= 32) ? kNumCUs : 2 * kNumCUs;
+  if (units > pages_bound) units = pages_bound;
+  if (units < 1) units = 1;
+  return (int)units;
+}
+
+// One partial result per (unit, sequence) piece.  Pieces are numbered unit + sequence, which grows
+// strictly along the page order, so units + batch slots always suffice.
+size_t workspace_bytes(int batch, int heads, int units) {
+  const size_t parts = ((size_t)units + (size_t)batch) * (size_t)heads;
+  return parts * (size_t)kDc * sizeof(float) + parts * 2 * sizeof(float);
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+static bool valid_dtype(mla_dtype d) { return d == MLA_BF16 || d == MLA_F32; }
+static bool valid_heads(int h) { return h == 16 || h == 32 || h == 64 || h == 128; }
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is null";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: invalid or inconsistent size";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown dtype";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: page_size must be 64, heads in {16,32,64,128}";
+    case MLA_ERR_BLOCK_TABLE: return "MLA_ERR_BLOCK_TABLE: block table entry out of range";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch failed";
+    default: return "unknown mla_status";
+  }
+}
+
+int mla_abi_version(void) { return 100; }
+
+size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
+                                 mla_dtype dtype) {
+  if (batch < 0 || max_blocks_per_seq < 1 || num_splits < 0 || !valid_heads(num_heads) ||
+      !valid_dtype(dtype))
+    return 0;
+  const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq);
+  return workspace_bytes(batch, num_heads, units);
+}
+
+mla_status mla_cache_append(void* kv_cache, int num_pages, int page_size, const int32_t* block_table,
+                            int max_blocks_per_seq, const int32_t* positions, const void* c_new,
+                            const void* kpe_new, int batch, mla_dtype dtype, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (num_pages < 1) return MLA_ERR_SHAPE;
+  if (!kv_cache || !block_table || !positions || !c_new || !kpe_new) return MLA_ERR_NULL;
+  hipError_t e = launch_append(kv_cache, block_table, max_blocks_per_seq, positions, c_new, kpe_new,
+                               batch, dtype == MLA_F32, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_absorb_q(const void* q, const void* w_uk, void* q_abs, int batch, int num_heads,
+                        mla_dtype dtype, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (batch < 0) return MLA_ERR_SHAPE;
+  if (!valid_heads(num_heads)) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!q || !w_uk || !q_abs) return MLA_ERR_NULL;
+  hipError_t e = launch_absorb(q, w_uk, q_abs, batch, num_heads, dtype == MLA_F32, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_out_proj(const void* o_lat, const void* w_uv, void* out, int batch, int num_heads,
+                        mla_dtype dtype, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (batch < 0) return MLA_ERR_SHAPE;
+  if (!valid_heads(num_heads)) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  hipError_t e = launch_out_proj(o_lat, w_uv, out, batch, num_heads, dtype == MLA_F32, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                      const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                      int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
+                      void* workspace, size_t workspace_bytes_given, int num_splits, mla_dtype dtype,
+                      hipStream_t stream) {
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (!valid_heads(num_heads)) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1 || num_splits < 0) return MLA_ERR_SHAPE;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q_abs || !kv_cache || !block_table || !seq_lens || !o_lat) return MLA_ERR_NULL;
+  const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq);
+  const size_t need = workspace_bytes(batch, num_heads, units);
+  if (!workspace || workspace_bytes_given < need) return MLA_ERR_WORKSPACE;
+
+  DecodeParams p;
+  p.q_abs = q_abs;
+  p.cache = static_cast<const uint16_t*>(kv_cache);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.o_lat = o_lat;
+  p.lse = lse;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + ((size_t)units + batch) * num_heads * kDc;
+  p.num_pages = num_pages;
+  p.max_blocks = max_blocks_per_seq;
+  p.batch = batch;
+  p.heads = num_heads;
+  p.num_units = units;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = launch_decode(p, dtype == MLA_F32, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

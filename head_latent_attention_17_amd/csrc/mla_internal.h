@@ -1,0 +1,50 @@
+// Internal interface between the C-ABI layer (mla_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDc = 512;      // latent width
+constexpr int kDr = 64;       // decoupled RoPE width
+constexpr int kDnope = 128;   // per-head content query/key width
+constexpr int kDv = 128;      // per-head value width
+constexpr int kRow = 576;     // cached numbers per token
+constexpr int kQdim = 192;    // [q_nope | q_pe]
+constexpr int kPage = 64;     // tokens per page
+constexpr int kNumCUs = 256;  // MI355X compute units (used only to pick the automatic split)
+
+// Everything a decode launch needs.  Pointers are device pointers.
+struct DecodeParams {
+  const void* q_abs;
+  const uint16_t* cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o_lat;
+  float* lse;          // may be null
+  float* ws_o;         // [units + batch][heads][512] fp32 un-normalised partial outputs
+  float* ws_ml;        // [units + batch][heads][2] fp32 (base-2 reference max, softmax sum)
+  int num_pages;
+  int max_blocks;
+  int batch;
+  int heads;
+  int num_units;
+  float scale_log2;    // softmax_scale * log2(e)
+};
+
+int auto_units(int batch, int heads, int max_blocks);
+size_t workspace_bytes(int batch, int heads, int units);
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_append(void* cache, const int32_t* block_table, int max_blocks,
+                         const int32_t* positions, const void* c_new, const void* kpe_new,
+                         int batch, bool f32, hipStream_t s);
+hipError_t launch_absorb(const void* q, const void* w_uk, void* q_abs, int batch, int heads,
+                         bool f32, hipStream_t s);
+hipError_t launch_out_proj(const void* o_lat, const void* w_uv, void* out, int batch, int heads,
+                           bool f32, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, bool f32, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,141 @@
+/*
+ * mla.h -- C ABI of libmla: Multi-head Latent Attention (MLA) decode over a paged latent cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (DeepSeek-V2, as the "DeepSeek-V2" explainer on aiany.app lays it out):
+ *   - Step 5, eq. 9: every token leaves one latent note c (d_c = 512 numbers) per layer; per-head
+ *     keys and values are functions of it, k_h = W_UK[h] c and v_h = W_UV[h]^T c.
+ *   - Step 6: a score q_nope . k_h equals (W_UK[h]^T q_nope) . c, so the query is moved into latent
+ *     space once and the keys are never built; W_UV is applied after the weighted sum.
+ *   - Step 7: position rides a separate 64-number rotated key k^R shared by all heads, scored by a
+ *     per-head 64-number q^R; the two scores add inside the softmax.
+ *   - Step 8: the cache therefore holds 512 + 64 = 576 numbers per token per layer.
+ * The pages give no API; the arguments below follow the problem as posed there: a cache of
+ * per-token notes plus RoPE strips, addressed through a block table, per-sequence lengths and a
+ * softmax scale.
+ *
+ * Fixed sizes: d_c = 512, d_R = 64, d_nope = d_v = 128, cache row = 576, page = 64 tokens.
+ *
+ * Layouts (all row-major, all device memory owned by the caller):
+ *   kv_cache     bf16 [num_pages][64][576]; row = [c (512) | k^R (64)], 1152 bytes
+ *   block_table  int32 [batch][max_blocks_per_seq]; token t of sequence b lives in page
+ *                block_table[b][t / 64], slot t % 64.  Entries for blocks a sequence does not use
+ *                are never read (any value, -1 by convention).
+ *   q            [batch][heads][192] = [q_nope (128) | q^R (64)]; q^R and k^R arrive rotated
+ *   w_uk         [heads][128][512]  (k_h = W_UK[h] c)
+ *   w_uv         [heads][512][128]  (v_h = c^T W_UV[h])
+ *   q_abs        [batch][heads][576] = [W_UK[h]^T q_nope | q^R]
+ *   o_lat        [batch][heads][512] = sum_t p_t c_t
+ *   out          [batch][heads][128] = o_lat W_UV[h]
+ *   lse          fp32 [batch][heads]: natural log of sum_t exp(scale * q_abs . row_t)
+ * Element type of q, w_uk, w_uv, q_abs, o_lat, out, c_new, kpe_new: bf16 for MLA_BF16, fp32 for
+ * MLA_F32 (a debug mode with fp32 intermediates; the cache stays bf16 in both modes).
+ *
+ * Conventions:
+ *   - Every call is asynchronous on the caller's stream (0 = the null stream).  The library never
+ *     synchronises and never allocates; scratch memory comes from a caller workspace.
+ *   - Every entry point validates its arguments on the host before launching anything and returns a
+ *     negative mla_status on error, without touching any buffer.  Launch failures are reported as
+ *     MLA_ERR_HIP.  Nothing is thrown across the ABI.
+ *   - Device-side contents (block-table entries, lengths) are trusted: an entry outside
+ *     [0, num_pages) or a length above max_blocks_per_seq * 64 is undefined behaviour.
+ *   - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,         /* a required pointer is null */
+  MLA_ERR_SHAPE = -2,        /* a size is negative, zero where it must not be, or inconsistent */
+  MLA_ERR_DTYPE = -3,        /* unknown mla_dtype */
+  MLA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than mla_decode_workspace_size() */
+  MLA_ERR_UNSUPPORTED = -5,  /* page_size != 64, or heads not in {16, 32, 64, 128} */
+  MLA_ERR_BLOCK_TABLE = -6,  /* reserved for a device-side block-table check */
+  MLA_ERR_HIP = -7           /* a HIP launch failed */
+} mla_status;
+
+typedef enum { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+#define MLA_D_C 512
+#define MLA_D_R 64
+#define MLA_D_NOPE 128
+#define MLA_D_V 128
+#define MLA_ROW 576
+#define MLA_PAGE_SIZE 64
+
+/* Human-readable name of a status code; never null. */
+const char* mla_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int mla_abi_version(void);
+
+/*
+ * Bytes of workspace mla_decode needs for these sizes (0 on invalid arguments).
+ * num_splits is the number of equal page ranges the batch's pages are cut into (0 = automatic: the
+ * value mla_decode would choose).  The result does not depend on the sequence lengths.
+ */
+size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
+                                 mla_dtype dtype);
+
+/*
+ * Append one token per sequence to the paged cache (explainer Step 2: the note of a token already
+ * read never changes, so it is stored once; Step 8: the stored row is [c | k^R]).
+ * For each b: row [c_new[b] (512) | kpe_new[b] (64)] is copied bit for bit to logical position
+ * positions[b] (the length before the append): page block_table[b][positions[b] / 64], slot
+ * positions[b] % 64.  c_new / kpe_new are bf16 for MLA_BF16 and fp32 holding bf16-representable
+ * values for MLA_F32 (their low 16 bits must then be zero; they are dropped).  seq_lens is not
+ * touched: the caller adds one after the append.  Sequences appending to the same page slot race.
+ */
+mla_status mla_cache_append(void* kv_cache, int num_pages, int page_size, const int32_t* block_table,
+                            int max_blocks_per_seq, const int32_t* positions, const void* c_new,
+                            const void* kpe_new, int batch, mla_dtype dtype, hipStream_t stream);
+
+/*
+ * Absorb the content query into latent space (explainer Step 6):
+ *   q_abs[b][h][0:512]   = q[b][h][0:128] @ W_UK[h]     (fp32 accumulation)
+ *   q_abs[b][h][512:576] = q[b][h][128:192]             (q^R passes through, explainer Step 7)
+ */
+mla_status mla_absorb_q(const void* q, const void* w_uk, void* q_abs, int batch, int num_heads,
+                        mla_dtype dtype, hipStream_t stream);
+
+/*
+ * Decode attention in latent space for one query per sequence, all heads (explainer Steps 6-7):
+ *   s_t   = softmax_scale * (q_abs[b][h] . row_t),  t = 0 .. seq_lens[b]-1   (576-long dot)
+ *   o_lat = sum_t softmax(s)_t * c_t                                          (512 wide)
+ *   lse   = log sum_t exp(s_t)                                                (natural log)
+ * The pages of all sequences are cut into num_splits equal ranges (0 = automatic); each range is
+ * reduced by one workgroup and sequences cut across ranges are combined with a log-sum-exp merge.
+ * Results do not depend on num_splits beyond rounding; equal arguments give bit-identical results.
+ * A sequence of length 0 gives o_lat = 0 and lse = -inf.  lse may be null.
+ * workspace must hold mla_decode_workspace_size(batch, num_heads, max_blocks_per_seq, num_splits,
+ * dtype) bytes; its contents on entry are ignored.
+ */
+mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                      const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                      int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
+                      void* workspace, size_t workspace_bytes, int num_splits, mla_dtype dtype,
+                      hipStream_t stream);
+
+/*
+ * Per-head value up-projection after the weighted sum (explainer Step 6: W_UV is applied on the
+ * output side instead of to every cached token):
+ *   out[b][h][:] = o_lat[b][h][:] @ W_UV[h]      (512 -> 128, fp32 accumulation)
+ */
+mla_status mla_out_proj(const void* o_lat, const void* w_uv, void* out, int batch, int num_heads,
+                        mla_dtype dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/mla.h declares,
+and its host-side validation returns the documented status codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def _lib():
+    from head_latent_attention_17_amd import _lib as L
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_path_calls():
+    names = declared_functions()
+    for n in ("mla_cache_append", "mla_absorb_q", "mla_decode", "mla_out_proj"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(declared_functions()) == set(L.EXPORTS)
+
+
+def test_status_strings_and_version():
+    L = _lib()
+    assert L.mla_abi_version() == 100
+    for code, name in L.STATUS.items():
+        assert L.mla_status_string(code).startswith(name)
+    assert "unknown" in L.mla_status_string(12345)
+
+
+def test_workspace_size_formula():
+    L = _lib()
+    # (units + batch) pieces * heads * (512 partial outputs + max + sum) * 4 bytes
+    assert L.mla_decode_workspace_size(4, 128, 2048, 64) == (64 + 4) * 128 * 514 * 4
+    assert L.mla_decode_workspace_size(4, 128, 2048, 0) == (256 + 4) * 128 * 514 * 4
+    assert L.mla_decode_workspace_size(1, 16, 3, 0) == (3 + 1) * 16 * 514 * 4   # never more units than pages
+    assert L.mla_decode_workspace_size(4, 100, 2048, 0) == 0                  # unsupported heads
+    assert L.mla_decode_workspace_size(4, 128, 0, 0) == 0
+    assert L.mla_decode_workspace_size(4, 128, 8, -1) == 0
+    assert L.mla_decode_workspace_size(4, 128, 8, 0, 7) == 0                  # unknown dtype
+
+
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def _decode(L, **kw):
+    a = dict(q_abs=FAKE, cache=FAKE, num_pages=16, page_size=64, bt=FAKE, max_blocks=16, lens=FAKE,
+             batch=1, heads=16, scale=0.07, o_lat=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30,
+             splits=0, dtype=0)
+    a.update(kw)
+    return L.lib.mla_decode(a["q_abs"], a["cache"], a["num_pages"], a["page_size"], a["bt"],
+                            a["max_blocks"], a["lens"], a["batch"], a["heads"], a["scale"],
+                            a["o_lat"], a["lse"], a["ws"], a["ws_bytes"], a["splits"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), -3),
+    (dict(page_size=32), -5),
+    (dict(heads=100), -5),
+    (dict(batch=-1), -2),
+    (dict(max_blocks=0), -2),
+    (dict(splits=-3), -2),
+    (dict(scale=0.0), -2),
+    (dict(scale=float("nan")), -2),
+    (dict(q_abs=None), -1),
+    (dict(cache=None), -1),
+    (dict(lens=None), -1),
+    (dict(o_lat=None), -1),
+    (dict(ws=None), -4),
+    (dict(ws_bytes=10), -4),
+])
+def test_decode_validation(kw, status):
+    assert _decode(_lib(), **kw) == status
+
+
+def test_empty_batch_is_a_no_op():
+    L = _lib()
+    assert _decode(L, batch=0, q_abs=None, cache=None, ws=None) == 0
+    assert L.lib.mla_absorb_q(None, None, None, 0, 128, 0, None) == 0
+    assert L.lib.mla_out_proj(None, None, None, 0, 128, 0, None) == 0
+    assert L.lib.mla_cache_append(None, 0, 64, None, 1, None, None, None, 0, 0, None) == 0
+
+
+def test_projection_and_append_validation():
+    L = _lib()
+    assert L.lib.mla_absorb_q(FAKE, FAKE, FAKE, 2, 96, 0, None) == -5
+    assert L.lib.mla_absorb_q(FAKE, None, FAKE, 2, 128, 0, None) == -1
+    assert L.lib.mla_absorb_q(FAKE, FAKE, FAKE, 2, 128, 9, None) == -3
+    assert L.lib.mla_out_proj(FAKE, FAKE, None, 2, 128, 0, None) == -1
+    assert L.lib.mla_out_proj(FAKE, FAKE, FAKE, -2, 128, 0, None) == -2
+    assert L.lib.mla_cache_append(FAKE, 8, 16, FAKE, 1, FAKE, FAKE, FAKE, 2, 0, None) == -5
+    assert L.lib.mla_cache_append(FAKE, 8, 64, FAKE, 1, None, FAKE, FAKE, 2, 0, None) == -1
+    assert L.lib.mla_cache_append(FAKE, 0, 64, FAKE, 1, FAKE, FAKE, FAKE, 2, 0, None) == -2
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    L = _lib()
+    x = torch.zeros(4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        L.mla_out_proj(x, x, x)

@@ -1,0 +1,176 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle, at small sizes that still
+span several 32-token tiles, several pages and a ragged tail; plus the exact cases: append bytes,
+the needle, page-permutation invariance, empty sequences and determinism."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import mla_oracle as O
+from tests.gpu_cases import BF16_TOL, F32_TOL, Gpu, act, host_inputs, rel_err, say, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 63, 64, 65, 127, 300, 1000]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    import head_latent_attention_17_amd as L
+    return L
+
+
+def _tol(f32):
+    return F32_TOL if f32 else BF16_TOL
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_append_is_bit_exact(lib, f32):
+    wl = synth.make_custom([0, 5, 63, 64, 65, 200], heads=16, seed=21, append=True)
+    say("append", wl.lens.tolist(), "f32" if f32 else "bf16")
+    g = Gpu(wl, f32=f32)
+    before = synth.to_numpy_u16(g.cache.view(torch.int16))
+    lib.mla_cache_append(g.cache, g.bt, g.lens, g.c_new, g.kpe_new)
+    torch.cuda.synchronize()
+    after = synth.to_numpy_u16(g.cache.view(torch.int16))
+    rows = synth.to_numpy_u16(synth.new_rows(wl))
+    want = O.append_rows(before, wl.block_table, wl.lens, rows)
+    assert np.array_equal(after, want)
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("f32", [False, True])
+def test_decode_matches_oracle(lib, heads, f32):
+    wl = synth.make_custom(RAGGED, heads=heads, seed=30 + heads)
+    say("decode", heads, "f32" if f32 else "bf16")
+    g = Gpu(wl, f32=f32)
+    g.step(lib, q_abs_from_absorb=False)
+    torch.cuda.synchronize()
+    hi = host_inputs(wl, 0, range(wl.batch))
+    o_ref, lse_ref = O.latent_decode_batch(hi["q_lat"], hi["cache"], wl.block_table, wl.attended_lens, wl.scale)
+    e_o = rel_err(to_host_f64(g.o_lat), o_ref)
+    e_l = float(np.abs(g.lse.cpu().numpy() - lse_ref).max() / np.abs(lse_ref).max())
+    say(f"  o_lat err {e_o:.3e}  lse err {e_l:.3e}")
+    assert e_o <= _tol(f32) and e_l <= _tol(f32)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64, 0])
+def test_split_count_invariance(lib, splits):
+    wl = synth.make_custom(RAGGED + [4096, 2], heads=128, seed=41)
+    say("splits", splits)
+    g = Gpu(wl)
+    g.step(lib, splits=splits, q_abs_from_absorb=False)
+    torch.cuda.synchronize()
+    hi = host_inputs(wl, 0, range(wl.batch))
+    o_ref, lse_ref = O.latent_decode_batch(hi["q_lat"], hi["cache"], wl.block_table, wl.attended_lens,
+                                           wl.scale, heads=range(0, 128, 9))
+    hs = list(range(0, 128, 9))
+    e = rel_err(to_host_f64(g.o_lat)[:, hs], o_ref[:, hs])
+    say(f"  err {e:.3e}")
+    assert e <= BF16_TOL
+    assert np.abs(g.lse.cpu().numpy()[:, hs] - lse_ref[:, hs]).max() < 1e-2
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_end_to_end_with_append_matches_decompressed_oracle(lib, f32):
+    wl = synth.make_custom([1, 64, 200, 777], heads=128, seed=51, append=True)
+    say("end-to-end", "f32" if f32 else "bf16")
+    g = Gpu(wl, f32=f32)
+    g.step(lib)
+    torch.cuda.synchronize()
+    hi = host_inputs(wl, 0, range(wl.batch))
+    out_ref, lse_ref = O.decode_reference(hi["q"], hi["cache"], wl.block_table, wl.attended_lens,
+                                          hi["w_uk"], hi["w_uv"], wl.scale)
+    q_abs_ref = O.absorb_batch(hi["q"], hi["w_uk"])
+    e_q = rel_err(to_host_f64(g.q_abs), q_abs_ref)
+    e_out = rel_err(to_host_f64(g.out), out_ref)
+    e_l = float(np.abs(g.lse.cpu().numpy() - lse_ref).max() / np.abs(lse_ref).max())
+    say(f"  q_abs {e_q:.3e} out {e_out:.3e} lse {e_l:.3e}")
+    assert e_q <= _tol(f32) and e_out <= _tol(f32) and e_l <= _tol(f32)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_out_proj_matches_oracle(lib, f32):
+    wl = synth.make_custom([5] * 9, heads=64, seed=61)
+    say("out_proj", "f32" if f32 else "bf16")
+    g = Gpu(wl, f32=f32)
+    o_in = g.q_lat_in[..., :synth.D_C].contiguous()   # any seeded bf16 input of the right shape
+    lib.mla_out_proj(o_in, g.w_uv, g.out)
+    torch.cuda.synchronize()
+    _, w_uv = synth.weights(wl)
+    ref = O.out_proj_batch(synth.to_numpy_u16(synth.latent_queries(wl))[..., :synth.D_C],
+                           synth.to_numpy_u16(w_uv))
+    e = rel_err(to_host_f64(g.out), ref)
+    say(f"  err {e:.3e}")
+    assert e <= _tol(f32)
+
+
+def test_empty_sequences(lib):
+    wl = synth.make_custom([0, 70, 0, 5], heads=16, seed=71)
+    say("empty sequences")
+    g = Gpu(wl)
+    for splits in (0, 3):
+        g.o_lat.fill_(7.0)
+        g.step(lib, splits=splits, q_abs_from_absorb=False)
+        torch.cuda.synchronize()
+        o = g.o_lat.float().cpu()
+        assert torch.all(o[0] == 0) and torch.all(o[2] == 0)
+        assert torch.all(torch.isneginf(g.lse[0])) and torch.all(torch.isneginf(g.lse[2]))
+        assert torch.isfinite(o[1]).all() and torch.isfinite(o[3]).all()
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("splits", [0, 1, 7])
+def test_needle_is_bit_exact(lib, f32, splits):
+    """A RoPE-only query matching one token's k^R: every other weight underflows to exactly zero, so
+    o_lat must equal that token's latent note bit for bit, wherever the needle sits."""
+    L = 1000
+    wl = synth.make_custom([L, L], heads=16, seed=81)
+    g = Gpu(wl, f32=f32)
+    base = g.cache.view(torch.int16).cpu()
+    t = np.arange(L)
+    for star in (0, 31, 32, 63, 64, 500, L - 1):
+        say("needle", star, splits, "f32" if f32 else "bf16")
+        cache = base.clone()
+        for b in range(wl.batch):
+            pages = torch.as_tensor(wl.block_table[b, t // 64]).long()
+            slots = torch.as_tensor(t % 64).long()
+            vals = torch.full((L,), -16512, dtype=torch.int16)      # -1.0 (0xBF80)
+            vals[star] = 0x3F80                                        # +1.0
+            cache[pages, slots, synth.D_C] = vals
+        g.cache.view(torch.int16).copy_(cache)
+        q = torch.zeros(wl.batch, wl.heads, synth.ROW, dtype=torch.float32)
+        q[:, :, synth.D_C] = 1000.0
+        qa = q.cuda() if f32 else q.to(torch.bfloat16).cuda()
+        lib.mla_decode(qa, g.cache, g.bt, g.attended, wl.scale, g.o_lat, g.lse, g.workspace(lib, splits), splits)
+        torch.cuda.synchronize()
+        got = g.o_lat.float().cpu()
+        for b in range(wl.batch):
+            page, slot = wl.block_table[b, star // 64], star % 64
+            want = (cache[page, slot, :synth.D_C].to(torch.int32) << 16).view(torch.float32)
+            assert torch.equal(got[b], want.expand(wl.heads, -1)), (b, star)
+
+
+def test_page_permutation_invariance_and_determinism(lib):
+    wl_s = synth.make_custom([700, 64, 130], heads=128, seed=91)
+    wl_c = synth.make_custom([700, 64, 130], heads=128, seed=91, shuffle=False)
+    say("permutation invariance")
+    gs = Gpu(wl_s)
+    gc = Gpu(wl_c)
+    # place the same logical rows in the contiguous layout
+    src = gs.cache.view(torch.int16)
+    dst = gc.cache.view(torch.int16)
+    for b in range(wl_s.batch):
+        for j in range(int((wl_s.block_table[b] >= 0).sum())):
+            dst[wl_c.block_table[b, j]] = src[wl_s.block_table[b, j]]
+    gc.q_lat_in.copy_(gs.q_lat_in)
+    outs = []
+    for g in (gs, gc, gs):
+        g.step(lib, q_abs_from_absorb=False)
+        torch.cuda.synchronize()
+        outs.append((g.o_lat.view(torch.int16).clone(), g.lse.clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l.view(torch.int32), outs[0][1].view(torch.int32))
