@@ -132,20 +132,21 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
 // Finishes every sequence: combines its pieces (one per work unit it touches, stored at slot
 // unit + sequence), divides by the softmax sum and writes o_lat and lse.
 //   M = max_s m_s;  w_s = 2^(m_s - M);  o = sum_s w_s o_s / sum_s w_s l_s;  lse = ln2 (M + log2 sum_s w_s l_s)
-// One workgroup per (sequence, 4 heads); 64 lanes per head, 8 latent dims per lane.
+// One workgroup per (sequence, 2 heads); 128 lanes per head, 4 latent dims per lane; the loop over
+// pieces keeps four loads in flight.
 template <typename OT>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int b = blockIdx.x;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 2 + (threadIdx.x >> 7);
+  const int d = (threadIdx.x & 127) * 4;
   const int len = p.seq_lens[b];
   const long long np = pages_of(len);
   OT* o = static_cast<OT*>(p.o_lat);
-  const size_t ob = ((size_t)b * p.heads + h) * kDc + lane * 8;
+  const size_t ob = ((size_t)b * p.heads + h) * kDc + d;
   if (np == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) Elem<OT>::store(o, ob + i, 0.f);
-    if (p.lse && lane == 0) p.lse[(size_t)b * p.heads + h] = -INFINITY;
+    for (int i = 0; i < 4; ++i) Elem<OT>::store(o, ob + i, 0.f);
+    if (p.lse && d == 0) p.lse[(size_t)b * p.heads + h] = -INFINITY;
     return;
   }
   const long long P = total_pages(p.seq_lens, p.batch);
@@ -153,31 +154,48 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int W = p.num_units;
   const int wf = unit_of_page(P, W, before);
   const int wl = unit_of_page(P, W, before + np - 1);
+  // Units that hold no page (possible only when there are more units than pages) wrote nothing.
+  auto live = [&](int w) { return unit_start(P, W, w) != unit_start(P, W, w + 1); };
+  auto slot = [&](int w) { return ((size_t)w + b) * p.heads + h; };
 
   float mx = -INFINITY;
-  for (int w = wf; w <= wl; ++w) {
-    if (unit_start(P, W, w) == unit_start(P, W, w + 1)) continue;
-    mx = fmaxf(mx, p.ws_ml[2 * (((size_t)w + b) * p.heads + h)]);
-  }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int w = wf; w <= wl; ++w)
+    if (live(w)) mx = fmaxf(mx, p.ws_ml[2 * slot(w)]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float sum = 0.f;
-  for (int w = wf; w <= wl; ++w) {
-    if (unit_start(P, W, w) == unit_start(P, W, w + 1)) continue;
-    const size_t part = ((size_t)w + b) * p.heads + h;
-    const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + 2 * part);
+  int w = wf;
+  for (; w + 3 <= wl; w += 4) {
+    float4 v[4];
+    float2 ml[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = *reinterpret_cast<const float4*>(p.ws_o + slot(w + u) * kDc + d);
+      ml[u] = *reinterpret_cast<const float2*>(p.ws_ml + 2 * slot(w + u));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!live(w + u)) continue;
+      const float wgt = exp2f(ml[u].x - mx);
+      sum = fmaf(wgt, ml[u].y, sum);
+      acc.x = fmaf(wgt, v[u].x, acc.x); acc.y = fmaf(wgt, v[u].y, acc.y);
+      acc.z = fmaf(wgt, v[u].z, acc.z); acc.w = fmaf(wgt, v[u].w, acc.w);
+    }
+  }
+  for (; w <= wl; ++w) {
+    if (!live(w)) continue;
+    const float4 v = *reinterpret_cast<const float4*>(p.ws_o + slot(w) * kDc + d);
+    const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + 2 * slot(w));
     const float wgt = exp2f(ml.x - mx);
     sum = fmaf(wgt, ml.y, sum);
-    const float4* src = reinterpret_cast<const float4*>(p.ws_o + part * kDc + lane * 8);
-    const float4 a = src[0], c = src[1];
-    acc[0] = fmaf(wgt, a.x, acc[0]); acc[1] = fmaf(wgt, a.y, acc[1]);
-    acc[2] = fmaf(wgt, a.z, acc[2]); acc[3] = fmaf(wgt, a.w, acc[3]);
-    acc[4] = fmaf(wgt, c.x, acc[4]); acc[5] = fmaf(wgt, c.y, acc[5]);
-    acc[6] = fmaf(wgt, c.z, acc[6]); acc[7] = fmaf(wgt, c.w, acc[7]);
+    acc.x = fmaf(wgt, v.x, acc.x); acc.y = fmaf(wgt, v.y, acc.y);
+    acc.z = fmaf(wgt, v.z, acc.z); acc.w = fmaf(wgt, v.w, acc.w);
   }
   const float inv = 1.f / sum;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) Elem<OT>::store(o, ob + i, acc[i] * inv);
-  if (p.lse && lane == 0) p.lse[(size_t)b * p.heads + h] = (mx + log2f(sum)) * 0.69314718055994531f;
+  Elem<OT>::store(o, ob, acc.x * inv);
+  Elem<OT>::store(o, ob + 1, acc.y * inv);
+  Elem<OT>::store(o, ob + 2, acc.z * inv);
+  Elem<OT>::store(o, ob + 3, acc.w * inv);
+  if (p.lse && d == 0) p.lse[(size_t)b * p.heads + h] = (mx + log2f(sum)) * 0.69314718055994531f;
 }
 
 template <typename T>
@@ -188,7 +206,7 @@ hipError_t launch_valu(const DecodeParams& p, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel<T>, dim3(p.batch, p.heads / 4), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(merge_kernel<T>, dim3(p.batch, p.heads / 2), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

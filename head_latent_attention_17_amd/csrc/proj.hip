@@ -1,8 +1,7 @@
-// Cache append and the two per-head projections around the latent decode:
+// Cache append, and the fp32 (debug-mode) versions of the two per-head projections around the
+// latent decode; the bf16 projections run on the matrix cores (proj_mfma.hip):
 //   absorb:   q_lat = q_nope @ W_UK[h]    (the query moved into latent space; DeepSeek-V2 explainer, Step 6)
 //   out-proj: out   = o_lat  @ W_UV[h]    (the value up-projection applied after the weighted sum, Step 6)
-// Both read each weight matrix once per launch and reuse it for the whole batch from LDS; they are
-// bound by the weight read (16.8 MB per matrix at 128 heads).
 #include "mla_device.h"
 
 namespace mla {
@@ -107,28 +106,27 @@ __global__ __launch_bounds__(256) void out_proj_valu_kernel(const T* o_lat, cons
   }
 }
 
+hipError_t launch_absorb_mfma(const void* q, const void* w_uk, void* q_abs, int batch, int heads,
+                              hipStream_t s);
+hipError_t launch_out_proj_mfma(const void* o_lat, const void* w_uv, void* out, int batch, int heads,
+                                hipStream_t s);
+
 hipError_t launch_absorb(const void* q, const void* w_uk, void* q_abs, int batch, int heads,
                          bool f32, hipStream_t s) {
-  const dim3 grid(heads, kDc / 64);
-  if (f32)
-    hipLaunchKernelGGL(absorb_valu_kernel<float>, grid, dim3(256), 0, s, (const float*)q,
-                       (const float*)w_uk, (float*)q_abs, batch, heads);
-  else
-    hipLaunchKernelGGL(absorb_valu_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)q,
-                       (const uint16_t*)w_uk, (uint16_t*)q_abs, batch, heads);
+  if (!f32) return launch_absorb_mfma(q, w_uk, q_abs, batch, heads, s);
+  // fp32 debug mode: vector ALU, fp32 products and sums
+  hipLaunchKernelGGL(absorb_valu_kernel<float>, dim3(heads, kDc / 64), dim3(256), 0, s,
+                     (const float*)q, (const float*)w_uk, (float*)q_abs, batch, heads);
   return hipGetLastError();
 }
 
 hipError_t launch_out_proj(const void* o_lat, const void* w_uv, void* out, int batch, int heads,
                            bool f32, hipStream_t s) {
-  const dim3 grid(heads, kDv / 32);
-  const size_t lds = (size_t)kDc * 32 * sizeof(float);
-  if (f32)
-    hipLaunchKernelGGL(out_proj_valu_kernel<float>, grid, dim3(256), lds, s, (const float*)o_lat,
-                       (const float*)w_uv, (float*)out, batch, heads);
-  else
-    hipLaunchKernelGGL(out_proj_valu_kernel<uint16_t>, grid, dim3(256), lds, s,
-                       (const uint16_t*)o_lat, (const uint16_t*)w_uv, (uint16_t*)out, batch, heads);
+  if (!f32) return launch_out_proj_mfma(o_lat, w_uv, out, batch, heads, s);
+  // fp32 debug mode: vector ALU, fp32 products and sums
+  hipLaunchKernelGGL(out_proj_valu_kernel<float>, dim3(heads, kDv / 32), dim3(256),
+                     (size_t)kDc * 32 * sizeof(float), s, (const float*)o_lat, (const float*)w_uv,
+                     (float*)out, batch, heads);
   return hipGetLastError();
 }
 
