@@ -132,21 +132,29 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
 // Finishes every sequence: combines its pieces (one per work unit it touches, stored at slot
 // unit + sequence), divides by the softmax sum and writes o_lat and lse.
 //   M = max_s m_s;  w_s = 2^(m_s - M);  o = sum_s w_s o_s / sum_s w_s l_s;  lse = ln2 (M + log2 sum_s w_s l_s)
-// One workgroup per (sequence, 2 heads); 128 lanes per head, 4 latent dims per lane; the loop over
-// pieces keeps four loads in flight.
-template <typename OT>
+// One workgroup of 256 lanes per (sequence, HPW heads): 256 / HPW lanes per head, HPW / 2 float4
+// of latent dims per lane.  Pieces are read a chunk at a time (16 float4 loads in flight per lane)
+// and folded in with a running maximum (the sums are rescaled when a chunk raises it), so the
+// partials are read once.  HPW trades parallelism (long sequences, few of them) against the fixed
+// per-workgroup cost (many short sequences).
+template <typename OT, int HPW>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
+  constexpr int kTPH = 256 / HPW;      // lanes per head
+  constexpr int kF4 = HPW / 2;         // float4 per lane per piece
+  constexpr int kChunk = 16 / kF4;     // pieces per chunk
   const int b = blockIdx.x;
-  const int h = blockIdx.y * 2 + (threadIdx.x >> 7);
-  const int d = (threadIdx.x & 127) * 4;
+  const int h = blockIdx.y * HPW + threadIdx.x / kTPH;
+  const int j = threadIdx.x % kTPH;
   const int len = p.seq_lens[b];
   const long long np = pages_of(len);
   OT* o = static_cast<OT*>(p.o_lat);
-  const size_t ob = ((size_t)b * p.heads + h) * kDc + d;
+  const size_t ob = ((size_t)b * p.heads + h) * kDc;
   if (np == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Elem<OT>::store(o, ob + i, 0.f);
-    if (p.lse && d == 0) p.lse[(size_t)b * p.heads + h] = -INFINITY;
+    for (int f = 0; f < kF4; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Elem<OT>::store(o, ob + 4 * (j + kTPH * f) + i, 0.f);
+    if (p.lse && j == 0) p.lse[(size_t)b * p.heads + h] = -INFINITY;
     return;
   }
   const long long P = total_pages(p.seq_lens, p.batch);
@@ -155,47 +163,65 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int wf = unit_of_page(P, W, before);
   const int wl = unit_of_page(P, W, before + np - 1);
   // Units that hold no page (possible only when there are more units than pages) wrote nothing.
-  auto live = [&](int w) { return unit_start(P, W, w) != unit_start(P, W, w + 1); };
+  const bool all_live = P >= W;
+  auto live = [&](int w) { return all_live || unit_start(P, W, w) != unit_start(P, W, w + 1); };
   auto slot = [&](int w) { return ((size_t)w + b) * p.heads + h; };
 
   float mx = -INFINITY;
-  for (int w = wf; w <= wl; ++w)
-    if (live(w)) mx = fmaxf(mx, p.ws_ml[2 * slot(w)]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float sum = 0.f;
-  int w = wf;
-  for (; w + 3 <= wl; w += 4) {
-    float4 v[4];
-    float2 ml[4];
+  float4 acc[kF4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v[u] = *reinterpret_cast<const float4*>(p.ws_o + slot(w + u) * kDc + d);
-      ml[u] = *reinterpret_cast<const float2*>(p.ws_ml + 2 * slot(w + u));
+  for (int f = 0; f < kF4; ++f) acc[f] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float sum = 0.f;
+  for (int w0 = wf; w0 <= wl; w0 += kChunk) {
+    float4 v[kChunk][kF4];
+    float2 ml[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (w0 + u <= wl) {
+        const float* src = p.ws_o + slot(w0 + u) * kDc + 4 * j;
+#pragma unroll
+        for (int f = 0; f < kF4; ++f) v[u][f] = *reinterpret_cast<const float4*>(src + 4 * kTPH * f);
+        ml[u] = *reinterpret_cast<const float2*>(p.ws_ml + 2 * slot(w0 + u));
+      }
+    }
+    bool use[kChunk];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      use[u] = w0 + u <= wl && live(w0 + u);
+      if (use[u]) cm = fmaxf(cm, ml[u].x);
+    }
+    if (cm > mx) {  // exp2(-inf) = 0 covers the first chunk
+      const float r = exp2f(mx - cm);
+      sum *= r;
+#pragma unroll
+      for (int f = 0; f < kF4; ++f) {
+        acc[f].x *= r; acc[f].y *= r; acc[f].z *= r; acc[f].w *= r;
+      }
+      mx = cm;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (!live(w + u)) continue;
+    for (int u = 0; u < kChunk; ++u) {
+      if (!use[u]) continue;
       const float wgt = exp2f(ml[u].x - mx);
       sum = fmaf(wgt, ml[u].y, sum);
-      acc.x = fmaf(wgt, v[u].x, acc.x); acc.y = fmaf(wgt, v[u].y, acc.y);
-      acc.z = fmaf(wgt, v[u].z, acc.z); acc.w = fmaf(wgt, v[u].w, acc.w);
+#pragma unroll
+      for (int f = 0; f < kF4; ++f) {
+        acc[f].x = fmaf(wgt, v[u][f].x, acc[f].x); acc[f].y = fmaf(wgt, v[u][f].y, acc[f].y);
+        acc[f].z = fmaf(wgt, v[u][f].z, acc[f].z); acc[f].w = fmaf(wgt, v[u][f].w, acc[f].w);
+      }
     }
   }
-  for (; w <= wl; ++w) {
-    if (!live(w)) continue;
-    const float4 v = *reinterpret_cast<const float4*>(p.ws_o + slot(w) * kDc + d);
-    const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + 2 * slot(w));
-    const float wgt = exp2f(ml.x - mx);
-    sum = fmaf(wgt, ml.y, sum);
-    acc.x = fmaf(wgt, v.x, acc.x); acc.y = fmaf(wgt, v.y, acc.y);
-    acc.z = fmaf(wgt, v.z, acc.z); acc.w = fmaf(wgt, v.w, acc.w);
-  }
   const float inv = 1.f / sum;
-  Elem<OT>::store(o, ob, acc.x * inv);
-  Elem<OT>::store(o, ob + 1, acc.y * inv);
-  Elem<OT>::store(o, ob + 2, acc.z * inv);
-  Elem<OT>::store(o, ob + 3, acc.w * inv);
-  if (p.lse && d == 0) p.lse[(size_t)b * p.heads + h] = (mx + log2f(sum)) * 0.69314718055994531f;
+#pragma unroll
+  for (int f = 0; f < kF4; ++f) {
+    const size_t e = ob + 4 * (j + kTPH * f);
+    Elem<OT>::store(o, e, acc[f].x * inv);
+    Elem<OT>::store(o, e + 1, acc[f].y * inv);
+    Elem<OT>::store(o, e + 2, acc[f].z * inv);
+    Elem<OT>::store(o, e + 3, acc[f].w * inv);
+  }
+  if (p.lse && j == 0) p.lse[(size_t)b * p.heads + h] = (mx + log2f(sum)) * 0.69314718055994531f;
 }
 
 template <typename T>
@@ -204,9 +230,16 @@ hipError_t launch_valu(const DecodeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Heads per merge workgroup: as many as keep at least one workgroup per compute unit.
 template <typename T>
 hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel<T>, dim3(p.batch, p.heads / 2), dim3(256), 0, s, p);
+  const long long rows = (long long)p.batch * p.heads;
+  if (rows >= 8LL * kNumCUs && p.heads % 8 == 0)
+    hipLaunchKernelGGL((merge_kernel<T, 8>), dim3(p.batch, p.heads / 8), dim3(256), 0, s, p);
+  else if (rows >= 4LL * kNumCUs && p.heads % 4 == 0)
+    hipLaunchKernelGGL((merge_kernel<T, 4>), dim3(p.batch, p.heads / 4), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((merge_kernel<T, 2>), dim3(p.batch, p.heads / 2), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
