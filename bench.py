@@ -3,12 +3,14 @@
 A step is the whole path for one batch: cache append (one new row per sequence), query absorption
 through W_UK, latent decode attention (with its split merge) and the W_UV out-projection.  Inputs are
 seeded synthetic data resident in HBM before timing starts.  Default workload: 32 sequences x 4,096
-cached tokens (+1 appended), 128 heads, 64-token pages with a shuffled block table.  The 151 MB
-cache fits in the 256 MB Infinity Cache, so the steps rotate through independent input sets.
+cached tokens, each appending its new token's row (so 4,097 are attended), 128 heads, 64-token pages
+with a shuffled block table.  The 151 MB cache fits in the 256 MB Infinity Cache, so the steps
+rotate through independent input sets.
 
 Prints one JSON line.  `value` is latent-cache GB/s over the whole step (tokens x 1,152 B / step
 time).  `roofline` reports the dominant call, mla_decode, timed with HIP events on the launch stream.
-`cpu_baseline` times the CPU oracle (decompressed form, float64) on a bounded sample.
+`cpu_baseline` times the CPU oracle (decompressed form, float64) on a bounded sample: whole
+sequences (gather + every head), in order, until about --cpu-seconds of work is done.
 
     python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
 """
@@ -43,6 +45,12 @@ def parse():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--profile-run", action="store_true",
+                    help="for counter runs: a few untimed steps, then mla_decode alone, then one "
+                         "1 GiB device copy that calibrates the byte counters; prints no JSON")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of "
+                         "--profile-run into profiles/traffic_<workload>.json; needs no GPU")
     return ap.parse_args()
 
 
@@ -69,42 +77,104 @@ def traffic_record(workload: str):
 
 
 def cpu_baseline(wl, seconds: float):
-    """The oracle (decompressed form, float64) on sequence 0: heads in order until `seconds` pass.
-    Rate = latent-cache bytes that the processed heads cover, per second."""
+    """The oracle (decompressed form, float64) on whole sequences of the same workload, in order,
+    until `seconds` of work are done.  Rate = latent-cache bytes of the finished sequences per
+    second of oracle time (gathering the rows included)."""
     from threadpoolctl import threadpool_info
 
     import synth
     from oracle import mla_oracle as O
 
-    b = 0
-    n = int(wl.attended_lens[b])
-    pages = wl.block_table[b][wl.block_table[b] >= 0]
-    cache = np.zeros((wl.num_pages, 64, 576), np.uint16)
-    cache[pages] = synth.to_numpy_u16(synth.cache_pages(wl, 0, pages=pages))
-    if wl.append:
-        cache = O.append_rows(cache, wl.block_table, wl.lens, synth.to_numpy_u16(synth.new_rows(wl)))
     q = synth.to_numpy_u16(synth.queries(wl))
     w_uk, w_uv = (synth.to_numpy_u16(w) for w in synth.weights(wl))
-    rows = O.bf16_to_f64(O.gather_rows(cache, wl.block_table, b, n))
     qf, wk, wv = O.bf16_to_f64(q), O.bf16_to_f64(w_uk), O.bf16_to_f64(w_uv)
-    t0 = time.perf_counter()
-    heads = 0
-    while heads < wl.heads:
-        O.decode_head(qf[b, heads], rows, wk[heads], wv[heads], wl.scale)
-        heads += 1
-        if time.perf_counter() - t0 >= seconds:
+    new = synth.to_numpy_u16(synth.new_rows(wl)) if wl.append else None
+    done_tokens, seqs, busy = 0, 0, 0.0
+    for b in range(wl.batch):
+        pages = wl.block_table[b][wl.block_table[b] >= 0]
+        cache = np.zeros((wl.num_pages, 64, 576), np.uint16)
+        cache[pages] = synth.to_numpy_u16(synth.cache_pages(wl, 0, pages=pages))
+        n = int(wl.attended_lens[b])
+        t0 = time.perf_counter()
+        if wl.append:
+            cache = O.append_rows(cache, wl.block_table[b:b + 1], wl.lens[b:b + 1], new[b:b + 1])
+        rows = O.bf16_to_f64(O.gather_rows(cache, wl.block_table, b, n))
+        for h in range(wl.heads):
+            O.decode_head(qf[b, h], rows, wk[h], wv[h], wl.scale)
+        busy += time.perf_counter() - t0
+        done_tokens += n
+        seqs += 1
+        if busy >= seconds:
             break
-    dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    gbs = n * ROW_BYTES * heads / wl.heads / dt / 1e9
+    gbs = done_tokens * ROW_BYTES / busy / 1e9
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"decode_reference (decompressed, float64) of sequence 0 ({n} tokens), "
-                      f"{heads} of {wl.heads} heads in {dt:.1f} s; host has "
-                      f"{len(os.sched_getaffinity(0))} usable cores"}
+            "sample": f"decode_reference (decompressed, float64): {seqs} of {wl.batch} sequences "
+                      f"({done_tokens} attended tokens, all {wl.heads} heads, append + gather included) "
+                      f"in {busy:.1f} s of oracle time; host has {len(os.sched_getaffinity(0))} usable cores"}
+
+
+CALIB_BYTES = 1 << 30   # the calibration copy: 1 GiB read and 1 GiB written
+
+
+def _pmc_rows(folder: str):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, workload: str):
+    """Per-call HBM bytes of mla_decode (decode kernel + merge kernel) from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the reading of the same counter on a copy of known size."""
+    out = {"workload": workload, "kernel_source_sha": kernel_source_sha(), "per_kernel": {}}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _pmc_rows(folder) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]
+                  or "copy" in r["Kernel_Name"].lower()]
+        calib = max(copies) if copies else 0.0
+        if calib < 0.5 * CALIB_BYTES:
+            raise SystemExit(f"{counter}: no calibration copy found in {folder}")
+        scale = CALIB_BYTES / calib
+        total = 0.0
+        for tag in ("decode_mfma_kernel", "merge_kernel"):
+            vals = [float(r["Counter_Value"]) * 1024 for r in rows if tag in r["Kernel_Name"]]
+            if not vals:
+                raise SystemExit(f"{counter}: no {tag} dispatch in {folder}")
+            avg = sum(vals) / len(vals) * scale
+            out["per_kernel"].setdefault(tag, {})[counter] = {"dispatches": len(vals), "bytes": round(avg)}
+            total += avg
+        out[counter.lower() + "_scale"] = round(scale, 5)
+        out[counter.lower().replace("_size", "") + "_bytes_per_call"] = round(total)
+    out["bytes_per_call"] = out["fetch_bytes_per_call"] + out["write_bytes_per_call"]
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+def bench_workload(config: int):
+    """The timed workload: the numbered configuration, with one appended row per sequence when the
+    configuration itself has none (a decode step appends the new token before attending)."""
+    import synth
+
+    wl = synth.make_config(config)
+    if wl.append or wl.layers > 1:
+        return wl
+    return synth.make_custom(wl.lens, wl.heads, wl.seed, shuffle=config != 1, append=True,
+                             name=wl.name + "+append")
 
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, bench_workload(args.config).name)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
@@ -118,7 +188,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    wl = synth.make_config(args.config)
+    wl = bench_workload(args.config)
     B, H = wl.batch, wl.heads
     layers = wl.layers
     N = wl.tokens                           # attended tokens per layer
@@ -171,6 +241,21 @@ def main():
 
     print(f"bench: {wl.name}, {N} tokens per layer, {layers} layer(s), {sets} input set(s)",
           file=sys.stderr, flush=True)
+    if args.profile_run:
+        for i in range(args.warmup):
+            step(i)
+        d = inst[0]
+        for _ in range(args.steps):
+            lib.mla_decode(q_abs, d["cache"], bt, att, wl.scale, o_lat, lse, ws, args.splits)
+        torch.cuda.synchronize()
+        del inst
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profile run done: {args.steps} mla_decode calls, one {CALIB_BYTES} B copy", file=sys.stderr,
+              flush=True)
+        return
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -197,7 +282,7 @@ def main():
         "data": "synthetic (seeded counter-based draws, bf16)",
         "config": {"workload": wl.name, "batch": B, "heads": H, "layers": layers,
                    "attended_tokens_per_layer": N, "page_size": 64, "input_sets": sets,
-                   "step": "append+absorb+decode+merge+out_proj" if wl.append or True else "",
+                   "step": ("append+" if wl.append else "") + "absorb+decode+merge+out_proj",
                    "num_splits": args.splits or "auto"},
         "tflops": round(step_flops / (ms_step * 1e-3) / 1e12, 3),
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),

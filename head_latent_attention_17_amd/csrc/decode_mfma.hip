@@ -48,7 +48,7 @@ constexpr int kBlocks = kTileTok / 8 * kCG;          // 36 blocks of 8 tokens x 
 constexpr int kTileBytes = kBlocks * 1024;           // 36,864
 constexpr int kStages = 4;                           // tiles it .. it+3
 constexpr float kRescaleThreshold = 8.0f;            // base-2 headroom before O is rescaled
-constexpr int kKAhead = 4;                           // score operand prefetch depth (k-steps)
+constexpr int kKAhead = 3;                           // score operand prefetch depth (k-steps)
 
 __device__ __forceinline__ int sigma(int x) { return ((x & 3) << 1) | ((x >> 2) & 1); }
 
@@ -99,6 +99,14 @@ __device__ __forceinline__ void mfma_a_drain(f32x16* o) {
 }
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Lane id as an opaque asm result: addresses derived from it where they are used cannot be hoisted
+// out of the tile loop, where they would hold VGPRs for its whole length.
+__device__ __forceinline__ int lane_id() {
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  return ln;
+}
 
 // Block-table entries and lengths are read through the constant address space so they become
 // scalar loads (lgkmcnt).  A vector load here would be ordered behind the in-flight LDS DMA and its
@@ -191,14 +199,24 @@ __device__ __forceinline__ void dma16(const char* gbase, unsigned voff, unsigned
 // than 32 tokens) re-reads its last valid row in place of the missing ones.
 template <int NW>
 __device__ __forceinline__ void issue_tile(const DecodeParams& p, const TileCursor& c,
-                                           LDS_AS char* stage, int wave, const int* lane_off) {
+                                           LDS_AS char* stage, int wave) {
   constexpr int kPer = kBlocks / NW;
   const int page = ld_const(p.block_table, (size_t)c.b * p.max_blocks + c.t / kPage);
   const int nt = min(kTileTok, c.t_end - c.t);
   const char* base = reinterpret_cast<const char*>(p.cache) +
                      ((size_t)page * kPage + (c.t % kPage)) * (kRow * 2);
   const unsigned lds = (unsigned)(uintptr_t)stage;
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
   if (nt == kTileTok) {
+    // slot (lane / 8, lane % 8) of a block holds token-in-group (lane / 8) ^ parity and
+    // chunk-in-group (lane % 8) ^ sigma(token-in-group)
+    int lane_off[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int tl = (ln >> 3) ^ par;
+      lane_off[par] = tl * (kRow * 2) + ((ln & 7) ^ sigma(tl)) * 16;
+    }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int blk = wave * kPer + j;
@@ -206,8 +224,6 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, const TileCurs
       dma16(base + tg * 8 * (kRow * 2) + cg * 128, (unsigned)lane_off[tg & 1], lds + blk * 1024);
     }
   } else {
-    int ln;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int blk = wave * kPer + j;
@@ -220,16 +236,24 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, const TileCurs
   }
 }
 
-// Score operand for k-step ks = 4 g + i: 8 consecutive latent dims of this lane's token.
-__device__ __forceinline__ bf16x8 k_operand(const LDS_AS char* tile, const int* k_base, int ks) {
-  return *reinterpret_cast<const LDS_AS bf16x8*>(tile + k_base[ks & 3] + 1024 * (ks >> 2));
+// Score operand for k-step ks: 8 consecutive latent dims (16 ks + 8 half ..) of token (lane % 32).
+// tk = tile + this lane's offset for ks = 0; the chunk 2 (ks % 4) + half of chunk group ks / 4 only
+// flips bits 5-6 of the offset (the swizzle XORs the chunk's upper bits with a lane constant) and
+// the chunk group is 1 KB per step.
+__device__ __forceinline__ bf16x8 k_operand(unsigned tk, int ks) {
+  const unsigned a = tk ^ (32u * (ks & 3));
+  return *reinterpret_cast<const LDS_AS bf16x8*>((const LDS_AS char*)(uintptr_t)a + 1024 * (ks >> 2));
 }
 
 // Output operand for d-block db and token half m: 8 tokens of one latent dim, gathered by two
-// 16-lane transposing reads (token rows 16 m + 8 r + 4 half + (lane % 16) / 4, r = 0, 1).
-__device__ __forceinline__ bf16x8 v_operand(const LDS_AS char* tile, const int* v_base, int db, int m) {
-  const LDS_AS char* p0 = tile + v_base[db & 1] + ((2 * m) * kCG + (db >> 1)) * 1024;
-  const LDS_AS char* p1 = tile + v_base[2 + (db & 1)] + ((2 * m + 1) * kCG + (db >> 1)) * 1024;
+// 16-lane transposing reads (token rows 16 m + 8 r + 4 half + (lane % 16) / 4, r = 0, 1).  tv =
+// tile + this lane's offset for db 0, r 0; odd d-blocks flip bit 6 of the offset (chunk bit 2), the
+// second token group of a half flips bit 7 (token-group parity in the swizzle), the column group
+// db / 2 and the token half are whole blocks (immediates).
+__device__ __forceinline__ bf16x8 v_operand(unsigned tv, int db, int m) {
+  const unsigned a = tv ^ (64u * (db & 1));
+  const LDS_AS char* p0 = (const LDS_AS char*)(uintptr_t)a + ((2 * m) * kCG + (db >> 1)) * 1024;
+  const LDS_AS char* p1 = (const LDS_AS char*)(uintptr_t)(a ^ 128u) + ((2 * m + 1) * kCG + (db >> 1)) * 1024;
   const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p0);
   const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p1);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -237,6 +261,7 @@ __device__ __forceinline__ bf16x8 v_operand(const LDS_AS char* tile, const int* 
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int kPer = kBlocks / NW;  // copies per wave per tile
   __shared__ __attribute__((aligned(1024))) char ring[kStages][kTileBytes];
 
   const int lane = threadIdx.x & 63;
@@ -251,49 +276,52 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   cp = ld;
   if (!cp.valid) return;
 
-  // DMA lane constants: slot (lane / 8, lane % 8) of a block holds token-in-group
-  // (lane / 8) ^ parity and chunk-in-group (lane % 8) ^ sigma(token-in-group).
-  int lane_off[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int tl = (lane >> 3) ^ par;
-    lane_off[par] = tl * (kRow * 2) + ((lane & 7) ^ sigma(tl)) * 16;
-  }
-  // Score operand bases: token l32, chunk 2 ks + half; per k-step the rest is an immediate.
-  int k_base[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) k_base[i] = tile_offset(l32, 2 * i + half);
-  // Transposing-read bases, [r][e]: token 8 r + 4 half + (lane % 16) / 4 of a 16-token half, chunk
-  // 4 e + 2 ((lane / 16) % 2) + (lane % 4) / 2 of a two-block column group, byte 8 (lane % 2); the
-  // token group itself is added as an immediate.
-  int v_base[4];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      v_base[r * 2 + e] = tile_offset(8 * r + 4 * half + ((lane & 15) >> 2),
-                                      4 * e + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
-                          8 * (lane & 1) - r * kCG * 1024;
+  // Score operand base: token l32, chunk half.  Output operand base: token 4 half + (lane % 16) / 4,
+  // chunk 2 ((lane / 16) % 2) + (lane % 4) / 2, byte 8 (lane % 2).  The per-step XORs above touch
+  // bits the swizzle alone sets, and every stage starts on a 1 KB boundary, so they may be applied
+  // after adding the stage base.
+  const unsigned k_off = (unsigned)tile_offset(l32, half);
+  const unsigned v_off = (unsigned)(tile_offset(4 * half + ((lane & 15) >> 2),
+                                                2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1));
 
   // Prologue: three tiles in flight.
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s) {
     if (ld.valid) {
-      issue_tile<NW>(p, ld, (LDS_AS char*)ring[s], wave, lane_off);
+      issue_tile<NW>(p, ld, (LDS_AS char*)ring[s], wave);
       ld.advance();
       ++issued;
     }
   }
+  // Waits until the copies of tile `t` (this wave's part) have landed, then for every wave.
+  // Vector loads complete in issue order: it is enough to let the tiles issued after it stay in
+  // flight.
+  auto tile_ready = [&](int t) __attribute__((always_inline)) {
+    const int younger = issued - t - 1;
+    if (younger >= 2) wait_vmcnt<(2 * kPer < 63 ? 2 * kPer : 63)>();
+    else if (younger == 1) wait_vmcnt<(kPer < 63 ? kPer : 63)>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+  // Refills the stage of the tile before `t` (every wave is past it) with the next tile.
+  auto refill = [&](int t) __attribute__((always_inline)) {
+    if (ld.valid) {
+      issue_tile<NW>(p, ld, (LDS_AS char*)ring[(t + kStages - 1) % kStages], wave);
+      ld.advance();
+      ++issued;
+    }
+  };
 
   const uint16_t* qa = static_cast<const uint16_t*>(p.q_abs);
   const float scale = p.scale_log2;
-  int it = 0;
+  int it = 0;  // tile index within the unit
   while (cp.valid) {  // one segment: the part of sequence b inside this unit
     const int b = cp.b;
     bf16x8 q[36];
     {
-      const uint16_t* qrow = qa + ((size_t)b * p.heads + head) * kRow + 8 * half;
+      const int ln = lane_id();
+      const uint16_t* qrow = qa + ((size_t)b * p.heads + wave * 32 + (ln & 31)) * kRow + 8 * (ln >> 5);
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
       // Wait here, once per segment: left to the compiler, the wait for Q would sit inside the tile
@@ -309,78 +337,107 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     float m_ref = -INFINITY;  // base-2 reference maximum (same in lanes l and l ^ 32)
     float l_sum = 0.f;        // this lane's share of the softmax denominator
     bool fresh = true;
-    bool last;
 
-    do {  // one 32-token tile
-      const int stage = it % kStages;
-      {
-        // This wave's DMA for tile `it` must have landed.  Vector loads complete in issue order, so
-        // it is enough to allow exactly the DMA of the tiles issued after it to stay in flight
-        // (later stores only make the wait longer).
-        constexpr int kPer = kBlocks / NW;
-        const int younger = issued - it - 1;
-        if (younger >= 2) wait_vmcnt<(2 * kPer < 63 ? 2 * kPer : 63)>();
-        else if (younger == 1) wait_vmcnt<(kPer < 63 ? kPer : 63)>();
-        else wait_vmcnt<0>();
-      }
-      __builtin_amdgcn_s_barrier();
-      const LDS_AS char* tile = (const LDS_AS char*)ring[stage];
-      // the first score operands go out before the DMA and cursor work, which covers their latency
+    // Scores of the segment's first tile, on their own.
+    f32x16 s_cur;
+    {
+      tile_ready(it);
+      const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[it % kStages] + k_off;
       bf16x8 ka[kKAhead + 1];
 #pragma unroll
-      for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tile, k_base, ks);
-      // Every wave is done with tile it-1: refill its stage.
-      if (ld.valid) {
-        issue_tile<NW>(p, ld, (LDS_AS char*)ring[(it + kStages - 1) % kStages], wave, lane_off);
-        ld.advance();
-        ++issued;
+      for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tk, ks);
+#pragma unroll
+      for (int ks = 0; ks < 36; ++ks) {
+        if (ks + kKAhead < 36) ka[(ks + kKAhead) % (kKAhead + 1)] = k_operand(tk, ks + kKAhead);
+        if (ks == 0) mfma_v_first(s_cur, ka[0], q[0]); else mfma_v(s_cur, ka[ks % (kKAhead + 1)], q[ks]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      mfma_v_drain(s_cur);
+    }
+
+    bool last;
+    do {  // tile `it`: its softmax and output product, overlapped with the next tile's scores
       const int nt = min(kTileTok, cp.t_end - cp.t);
       last = cp.last();
       cp.advance();
+      // The next tile must be in LDS before its scores start; the barrier also frees the stage of
+      // tile it - 1, which is refilled at once.
+      tile_ready(last ? it : it + 1);
+      refill(it);
 
-      // ---- scores: S^T = K . Q^T ---------------------------------------------------------------
-      f32x16 s;
+      // ---- softmax of tile it (base 2), lane = head, registers = tokens, spread over the next
+      // tile's score MFMAs -------------------------------------------------------------------------
+      float mt, ls = 0.f, alpha = 1.f;
+      bool rescale = false;
+      bf16x8 pb0, pb1;
+      auto softmax_step = [&](int k) __attribute__((always_inline)) {
+        if (k == 0) {
+          if (nt < kTileTok) {  // ragged tile: tokens past the end take no weight
+            const int hf = lane_id() >> 5;
 #pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        if (ks + kKAhead < 36) ka[(ks + kKAhead) % (kKAhead + 1)] = k_operand(tile, k_base, ks + kKAhead);
-        if (ks == 0) mfma_v_first(s, ka[0], q[0]); else mfma_v(s, ka[ks % (kKAhead + 1)], q[ks]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      // ---- softmax (base 2), lane = head, registers = tokens ------------------------------------
-      // The output operands of the first two d-blocks are requested first.
-      bf16x8 va[3][2];
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        va[db][0] = v_operand(tile, v_base, db, 0);
-        va[db][1] = v_operand(tile, v_base, db, 1);
-      }
-      mfma_v_drain(s);
-      if (nt < kTileTok) {  // ragged tile: tokens past the end take no weight
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int tok = (j >> 2) * 8 + half * 4 + (j & 3);
-          if (tok >= nt) s[j] = -INFINITY;
+            for (int j = 0; j < 16; ++j) {
+              const int tok = (j >> 2) * 8 + hf * 4 + (j & 3);
+              if (tok >= nt) s_cur[j] = -INFINITY;
+            }
+          }
+        } else if (k == 1) {
+          mt = fmaxf(fmaxf(fmaxf(s_cur[0], s_cur[1]), fmaxf(s_cur[2], s_cur[3])),
+                     fmaxf(fmaxf(s_cur[4], s_cur[5]), fmaxf(s_cur[6], s_cur[7])));
+        } else if (k == 2) {
+          mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(s_cur[8], s_cur[9]), fmaxf(s_cur[10], s_cur[11])),
+                               fmaxf(fmaxf(s_cur[12], s_cur[13]), fmaxf(s_cur[14], s_cur[15]))));
+        } else if (k == 3) {
+          mt = max_halves(mt) * scale;
+        } else if (k == 4) {
+          if (fresh) {
+            m_ref = mt;
+            fresh = false;
+          } else if (__ballot(mt > m_ref + kRescaleThreshold)) {
+            // Rare (the running maximum jumped by more than 2^8): the reference moves and O is
+            // scaled by alpha after the score MFMAs, before this tile's product is added.
+            const float m_new = fmaxf(m_ref, mt);
+            alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            l_sum *= alpha;
+            rescale = true;
+          }
+        } else if (k < 4 + 1 + 16) {
+          const int j = k - 5;
+          const float e = __builtin_amdgcn_exp2f(fmaf(s_cur[j], scale, -m_ref));
+          ls += e;
+          if (j < 8) pb0[j] = (__bf16)e; else pb1[j - 8] = (__bf16)e;
+        } else if (k == 21) {
+          l_sum += ls;
         }
+      };
+
+      if (!last) {
+        // scores of tile it + 1 into s_nxt, one softmax step of tile it after each MFMA
+        const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[(it + 1) % kStages] + k_off;
+        f32x16 s_nxt;
+        bf16x8 ka[kKAhead + 1];
+#pragma unroll
+        for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tk, ks);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) {
+          if (ks + kKAhead < 36) ka[(ks + kKAhead) % (kKAhead + 1)] = k_operand(tk, ks + kKAhead);
+          if (ks == 0) mfma_v_first(s_nxt, ka[0], q[0]); else mfma_v(s_nxt, ka[ks % (kKAhead + 1)], q[ks]);
+          softmax_step(ks);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_v_drain(s_nxt);
+        s_cur = s_nxt;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 22; ++k) softmax_step(k);
       }
-      float mt = fmaxf(fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))),
-                       fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-      mt = max_halves(mt) * scale;
-      if (fresh) {
-        m_ref = mt;
-        fresh = false;
-      } else if (__ballot(mt > m_ref + kRescaleThreshold)) {
-        // Rare (the running maximum jumped by more than 2^8): O is scaled before this tile's
-        // product is added.  The accumulators make a round trip through this piece's own
-        // workspace slot, which its final write overwrites anyway, so scaling them never holds
-        // more than one block in VGPRs.
-        const float m_new = fmaxf(m_ref, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-        m_ref = m_new;
-        l_sum *= alpha;
+
+      if (__builtin_expect(rescale, 0)) {
+        // The accumulators make a round trip through this piece's own workspace slot, which its
+        // final write overwrites anyway, so scaling them never holds more than one block in VGPRs.
         mfma_a_drain(o);
-        float* slot = p.ws_o + (((size_t)w + b) * p.heads + head) * kDc + 4 * half;
+        const int ln = lane_id();
+        float* slot = p.ws_o + (((size_t)w + b) * p.heads + wave * 32 + (ln & 31)) * kDc + 4 * (ln >> 5);
 #pragma unroll
         for (int db = 0; db < 16; ++db) {
 #pragma unroll
@@ -403,29 +460,33 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
           o[db] = t;
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      bf16x8 pb0, pb1;
-      {
-        float ls = 0.f;
+        // Q is read again from memory: redefining it here frees its 144 VGPRs for this block
+        // instead of leaving the register allocator to spill it around the hot loop.
+        const uint16_t* qrow = qa + ((size_t)b * p.heads + wave * 32 + (ln & 31)) * kRow + 8 * (ln >> 5);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[j], scale, -m_ref));
-          ls += e;
-          if (j < 8) pb0[j] = (__bf16)e; else pb1[j - 8] = (__bf16)e;
-        }
-        l_sum += ls;
+        for (int ks = 0; ks < 36; ++ks) q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+        wait_vmcnt<0>();
       }
 
-      // ---- output: O^T += V^T . P^T (operands two d-blocks ahead) -----------------------------
+      // ---- output of tile it: O^T += V^T . P^T (operands two d-blocks ahead) --------------------
+      {
+        const unsigned tv = (unsigned)(uintptr_t)(LDS_AS char*)ring[it % kStages] + v_off;
+        bf16x8 va[3][2];
 #pragma unroll
-      for (int db = 0; db < 16; ++db) {
-        if (db + 2 < 16) {
-          va[(db + 2) % 3][0] = v_operand(tile, v_base, db + 2, 0);
-          va[(db + 2) % 3][1] = v_operand(tile, v_base, db + 2, 1);
+        for (int db = 0; db < 2; ++db) {
+          va[db][0] = v_operand(tv, db, 0);
+          va[db][1] = v_operand(tv, db, 1);
         }
-        mfma_a(o[db], va[db % 3][0], pb0);
-        mfma_a(o[db], va[db % 3][1], pb1);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+          if (db + 2 < 16) {
+            va[(db + 2) % 3][0] = v_operand(tv, db + 2, 0);
+            va[(db + 2) % 3][1] = v_operand(tv, db + 2, 1);
+          }
+          mfma_a(o[db], va[db % 3][0], pb0);
+          mfma_a(o[db], va[db % 3][1], pb1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       ++it;
     } while (!last);
@@ -434,8 +495,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     // kernel divides by the softmax sum.
     const float l_tot = sum_halves(l_sum);
     mfma_a_drain(o);
-    const size_t part = ((size_t)w + b) * p.heads + head;
-    float* orow = p.ws_o + part * kDc + 4 * half;
+    const int ln = lane_id();
+    const size_t part = ((size_t)w + b) * p.heads + wave * 32 + (ln & 31);
+    float* orow = p.ws_o + part * kDc + 4 * (ln >> 5);
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
 #pragma unroll
@@ -443,7 +505,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         *reinterpret_cast<float4*>(orow + 32 * db + 8 * g) =
             make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
     }
-    if (half == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_ref, l_tot);
+    if (ln < 32) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_ref, l_tot);
   }
 }
 
