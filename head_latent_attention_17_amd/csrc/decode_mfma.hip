@@ -48,7 +48,14 @@ constexpr int kBlocks = kTileTok / 8 * kCG;          // 36 blocks of 8 tokens x 
 constexpr int kTileBytes = kBlocks * 1024;           // 36,864
 constexpr int kStages = 4;                           // tiles it .. it+3
 constexpr float kRescaleThreshold = 8.0f;            // base-2 headroom before O is rescaled
-constexpr int kKAhead = 3;                           // score operand prefetch depth (k-steps)
+#ifndef MLA_KAHEAD
+#define MLA_KAHEAD 3
+#endif
+#ifndef MLA_VAHEAD
+#define MLA_VAHEAD 4
+#endif
+constexpr int kKAhead = MLA_KAHEAD;                  // score operand prefetch depth (k-steps)
+constexpr int kVAhead = MLA_VAHEAD;                  // output operand prefetch depth (d-blocks)
 
 __device__ __forceinline__ int sigma(int x) { return ((x & 3) << 1) | ((x >> 2) & 1); }
 
@@ -78,6 +85,15 @@ __device__ __forceinline__ void mfma_v_first(f32x16& acc, const bf16x8& a, const
 __device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+// The same without the leading wait states, for loops whose MFMA operands come only from LDS reads
+// (waited by lgkmcnt), from registers no vector-ALU instruction wrote within the last two
+// instructions, and from the previous MFMA's accumulator (the hardware forwards that one).
+__device__ __forceinline__ void mfma_v_first_nw(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_nw(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
 __device__ __forceinline__ void mfma_v_drain(f32x16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
 }
@@ -85,6 +101,9 @@ __device__ __forceinline__ void mfma_v_drain(f32x16& acc) {
 // loop-carried 256-register accumulator into VGPR copies and spills.
 __device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_a_nw(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // acc = 0, produced by the matrix core itself (0 x 0 + 0) so it lands in AGPRs.
 __device__ __forceinline__ void mfma_a_zero(f32x16& acc, const bf16x8& zero) {
@@ -367,9 +386,15 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
 
       // ---- softmax of tile it (base 2), lane = head, registers = tokens, spread over the next
       // tile's score MFMAs -------------------------------------------------------------------------
-      float mt, ls = 0.f, alpha = 1.f;
+      float mt, ls0 = 0.f, ls1 = 0.f, alpha = 1.f;
       bool rescale = false;
       bf16x8 pb0, pb1;
+      // exponent j of the tile (token slot j of the accumulator), two running sums
+      auto softmax_exp = [&](int j) __attribute__((always_inline)) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s_cur[j], scale, -m_ref));
+        if (j & 1) ls1 += e; else ls0 += e;
+        if (j < 8) pb0[j] = (__bf16)e; else pb1[j - 8] = (__bf16)e;
+      };
       auto softmax_step = [&](int k) __attribute__((always_inline)) {
         if (k == 0) {
           if (nt < kTileTok) {  // ragged tile: tokens past the end take no weight
@@ -401,35 +426,29 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
             l_sum *= alpha;
             rescale = true;
           }
-        } else if (k < 4 + 1 + 16) {
-          const int j = k - 5;
-          const float e = __builtin_amdgcn_exp2f(fmaf(s_cur[j], scale, -m_ref));
-          ls += e;
-          if (j < 8) pb0[j] = (__bf16)e; else pb1[j - 8] = (__bf16)e;
-        } else if (k == 21) {
-          l_sum += ls;
+        } else if (k < 5 + 8) {
+          softmax_exp(k - 5);
         }
       };
 
+      f32x16 s_nxt;
       if (!last) {
         // scores of tile it + 1 into s_nxt, one softmax step of tile it after each MFMA
         const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[(it + 1) % kStages] + k_off;
-        f32x16 s_nxt;
         bf16x8 ka[kKAhead + 1];
 #pragma unroll
         for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tk, ks);
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) {
           if (ks + kKAhead < 36) ka[(ks + kKAhead) % (kKAhead + 1)] = k_operand(tk, ks + kKAhead);
-          if (ks == 0) mfma_v_first(s_nxt, ka[0], q[0]); else mfma_v(s_nxt, ka[ks % (kKAhead + 1)], q[ks]);
+          if (ks == 0) mfma_v_first_nw(s_nxt, ka[0], q[0]); else mfma_v_nw(s_nxt, ka[ks % (kKAhead + 1)], q[ks]);
           softmax_step(ks);
           __builtin_amdgcn_sched_barrier(0);
         }
         mfma_v_drain(s_nxt);
-        s_cur = s_nxt;
       } else {
 #pragma unroll
-        for (int k = 0; k < 22; ++k) softmax_step(k);
+        for (int k = 0; k < 13; ++k) softmax_step(k);
       }
 
       if (__builtin_expect(rescale, 0)) {
@@ -468,26 +487,28 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         wait_vmcnt<0>();
       }
 
-      // ---- output of tile it: O^T += V^T . P^T (operands two d-blocks ahead) --------------------
+      // ---- output of tile it: O^T += V^T . P^T, first the 16 tokens of pb0 for every d-block,
+      // then those of pb1 (the exponents of pb1 are computed during the first pass); operands
+      // kVAhead MFMAs ahead.
       {
         const unsigned tv = (unsigned)(uintptr_t)(LDS_AS char*)ring[it % kStages] + v_off;
-        bf16x8 va[3][2];
+        bf16x8 va[kVAhead + 1];
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          va[db][0] = v_operand(tv, db, 0);
-          va[db][1] = v_operand(tv, db, 1);
-        }
+        for (int i = 0; i < kVAhead; ++i) va[i] = v_operand(tv, i & 15, i >> 4);
 #pragma unroll
-        for (int db = 0; db < 16; ++db) {
-          if (db + 2 < 16) {
-            va[(db + 2) % 3][0] = v_operand(tv, db + 2, 0);
-            va[(db + 2) % 3][1] = v_operand(tv, db + 2, 1);
-          }
-          mfma_a(o[db], va[db % 3][0], pb0);
-          mfma_a(o[db], va[db % 3][1], pb1);
+        for (int i = 0; i < 32; ++i) {
+          const int nx = i + kVAhead;
+          if (nx < 32) va[nx % (kVAhead + 1)] = v_operand(tv, nx & 15, nx >> 4);
+          if (i == 0) mfma_a(o[0], va[0], pb0);                     // pb0 was just written
+          else if (i < 16) mfma_a_nw(o[i], va[i % (kVAhead + 1)], pb0);
+          else if (i == 16) mfma_a(o[0], va[16 % (kVAhead + 1)], pb1);
+          else mfma_a_nw(o[i & 15], va[i % (kVAhead + 1)], pb1);
+          if (i < 8) softmax_exp(8 + i);
+          if (i == 8) l_sum += ls0 + ls1;
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if (!last) s_cur = s_nxt;  // the second half of tile it's scores was needed until here
       ++it;
     } while (!last);
 
