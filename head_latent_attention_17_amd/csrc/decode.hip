@@ -5,6 +5,8 @@
 // is scored by one 576-long dot product with the latent-form query [W_UK^T q_nope | q^R] -- the
 // content score and the RoPE score add inside the softmax -- and the softmax weights average the
 // notes c_t.  The running softmax is kept in base 2: s' = s * scale * log2(e).
+#include <type_traits>
+
 #include "mla_device.h"
 
 namespace mla {
@@ -131,17 +133,18 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
 
 // Finishes every sequence: combines its pieces (one per work unit it touches, stored at slot
 // unit + sequence), divides by the softmax sum and writes o_lat and lse.
-//   M = max_s m_s;  w_s = 2^(m_s - M);  o = sum_s w_s o_s / sum_s w_s l_s;  lse = ln2 (M + log2 sum_s w_s l_s)
-// One workgroup of 256 lanes per (sequence, HPW heads): 256 / HPW lanes per head, HPW / 2 float4
-// of latent dims per lane.  Pieces are read a chunk at a time (16 float4 loads in flight per lane)
-// and folded in with a running maximum (the sums are rescaled when a chunk raises it), so the
-// partials are read once.  HPW trades parallelism (long sequences, few of them) against the fixed
-// per-workgroup cost (many short sequences).
-template <typename OT, int HPW>
+//   M = max_s m_s;  w_s = 2^(m_s - M);  o = sum_s w_s O_s / sum_s w_s l_s;  lse = ln2 (M + log2 sum_s w_s l_s)
+// where O_s is a piece's un-normalised sum (fp32 pieces) or l_s times its normalised bf16 sum
+// (bf16 pieces).  One workgroup of 256 lanes per (sequence, HPW heads): 256 / HPW lanes per head,
+// HPW / 2 groups of 4 latent dims per lane.  Pieces are read a chunk at a time (256 bytes in flight
+// per lane) and folded in with a running maximum (the sums are rescaled when a chunk raises it), so
+// the partials are read once.  HPW trades parallelism (long sequences, few of them) against the
+// fixed per-workgroup cost (many short sequences).
+template <typename OT, int HPW, bool PB>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   constexpr int kTPH = 256 / HPW;      // lanes per head
-  constexpr int kF4 = HPW / 2;         // float4 per lane per piece
-  constexpr int kChunk = 16 / kF4;     // pieces per chunk
+  constexpr int kF4 = HPW / 2;         // groups of 4 dims per lane per piece
+  constexpr int kChunk = (PB ? 32 : 16) / kF4;  // pieces per chunk: 256 bytes in flight per lane
   const int b = blockIdx.x;
   const int h = blockIdx.y * HPW + threadIdx.x / kTPH;
   const int j = threadIdx.x % kTPH;
@@ -173,14 +176,20 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   for (int f = 0; f < kF4; ++f) acc[f] = make_float4(0.f, 0.f, 0.f, 0.f);
   float sum = 0.f;
   for (int w0 = wf; w0 <= wl; w0 += kChunk) {
-    float4 v[kChunk][kF4];
+    // bf16 pieces stay packed (two registers per 4 dims) until they are used
+    typedef typename std::conditional<PB, uint2, float4>::type Raw;
+    Raw v[kChunk][kF4];
     float2 ml[kChunk];
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
       if (w0 + u <= wl) {
-        const float* src = p.ws_o + slot(w0 + u) * kDc + 4 * j;
+        const float* src = p.ws_o + slot(w0 + u) * kDc;
 #pragma unroll
-        for (int f = 0; f < kF4; ++f) v[u][f] = *reinterpret_cast<const float4*>(src + 4 * kTPH * f);
+        for (int f = 0; f < kF4; ++f) {
+          const int d = 4 * (j + kTPH * f);
+          if constexpr (PB) v[u][f] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + d);
+          else v[u][f] = *reinterpret_cast<const float4*>(src + d);
+        }
         ml[u] = *reinterpret_cast<const float2*>(p.ws_ml + 2 * slot(w0 + u));
       }
     }
@@ -204,11 +213,16 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     for (int u = 0; u < kChunk; ++u) {
       if (!use[u]) continue;
       const float wgt = exp2f(ml[u].x - mx);
-      sum = fmaf(wgt, ml[u].y, sum);
+      const float wl_s = wgt * ml[u].y;
+      sum += wl_s;
+      const float wo = PB ? wl_s : wgt;
 #pragma unroll
       for (int f = 0; f < kF4; ++f) {
-        acc[f].x = fmaf(wgt, v[u][f].x, acc[f].x); acc[f].y = fmaf(wgt, v[u][f].y, acc[f].y);
-        acc[f].z = fmaf(wgt, v[u][f].z, acc[f].z); acc[f].w = fmaf(wgt, v[u][f].w, acc[f].w);
+        float4 x;
+        if constexpr (PB) x = make_float4(bf16_lo(v[u][f].x), bf16_hi(v[u][f].x), bf16_lo(v[u][f].y), bf16_hi(v[u][f].y));
+        else x = v[u][f];
+        acc[f].x = fmaf(wo, x.x, acc[f].x); acc[f].y = fmaf(wo, x.y, acc[f].y);
+        acc[f].z = fmaf(wo, x.z, acc[f].z); acc[f].w = fmaf(wo, x.w, acc[f].w);
       }
     }
   }
@@ -230,29 +244,151 @@ hipError_t launch_valu(const DecodeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Merge for bf16 pieces: one workgroup per (sequence, head).  Its 256 lanes are four groups of 64;
+// lane l of group g holds latent dims 8 (l % 64) .. + 7 and folds in pieces g, g + 4, ... of the
+// sequence with a running maximum, all of its loads in flight together (one 16-byte load and one
+// 8-byte (max, sum) load per piece); the four groups are then combined through LDS.
+template <typename OT>
+__global__ __launch_bounds__(256) void merge_pieces_kernel(DecodeParams p) {
+  constexpr int kGroups = 4;
+  constexpr int kChunk = 16;  // pieces per group in flight
+  __shared__ float red_acc[kGroups][kDc];
+  __shared__ float red_ms[kGroups][2];
+  const int b = blockIdx.x;
+  const int h = blockIdx.y;
+  const int g = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63;
+  const int len = p.seq_lens[b];
+  const long long np = pages_of(len);
+  OT* o = static_cast<OT*>(p.o_lat);
+  const size_t ob = ((size_t)b * p.heads + h) * kDc;
+  if (np == 0) {
+    if (g == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Elem<OT>::store(o, ob + 8 * l + i, 0.f);
+      if (p.lse && l == 0) p.lse[(size_t)b * p.heads + h] = -INFINITY;
+    }
+    return;
+  }
+  const long long P = total_pages(p.seq_lens, p.batch);
+  const long long before = pages_before(p.seq_lens, b);
+  const int W = p.num_units;
+  const int wf = unit_of_page(P, W, before);
+  const int wl = unit_of_page(P, W, before + np - 1);
+  const bool all_live = P >= W;
+  auto live = [&](int w) { return all_live || unit_start(P, W, w) != unit_start(P, W, w + 1); };
+  auto slot = [&](int w) { return ((size_t)w + b) * p.heads + h; };
+
+  float mx = -INFINITY, sum = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int w0 = wf + g; w0 <= wl; w0 += kGroups * kChunk) {
+    uint4 v[kChunk];
+    float2 ml[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int w = w0 + kGroups * u;
+      if (w <= wl) {
+        v[u] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.ws_o + slot(w) * kDc) + 8 * l);
+        ml[u] = *reinterpret_cast<const float2*>(p.ws_ml + 2 * slot(w));
+      }
+    }
+    bool use[kChunk];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int w = w0 + kGroups * u;
+      use[u] = w <= wl && live(w);
+      if (use[u]) cm = fmaxf(cm, ml[u].x);
+    }
+    if (cm > mx) {
+      const float r = exp2f(mx - cm);
+      sum *= r;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= r;
+      mx = cm;
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (!use[u]) continue;
+      const float wl_s = exp2f(ml[u].x - mx) * ml[u].y;
+      sum += wl_s;
+      const uint32_t raw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wl_s, bf16_lo(raw[i]), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wl_s, bf16_hi(raw[i]), acc[2 * i + 1]);
+      }
+    }
+  }
+  // combine the four groups
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red_acc[g][8 * l + i] = acc[i];
+  if (l == 0) {
+    red_ms[g][0] = mx;
+    red_ms[g][1] = sum;
+  }
+  __syncthreads();
+  if (g == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) M = fmaxf(M, red_ms[q][0]);
+    float wq[kGroups], tot = 0.f;
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      wq[q] = exp2f(red_ms[q][0] - M);  // a group with no piece has max -inf and weight 0
+      tot += wq[q] * red_ms[q][1];
+    }
+    const float inv = 1.f / tot;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = 0.f;
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q) x = fmaf(wq[q], red_acc[q][8 * l + i], x);
+      Elem<OT>::store(o, ob + 8 * l + i, x * inv);
+    }
+    if (p.lse && l == 0) p.lse[(size_t)b * p.heads + h] = (M + log2f(tot)) * 0.69314718055994531f;
+  }
+}
+
 // Heads per merge workgroup: as many as keep at least one workgroup per compute unit.
-template <typename T>
+template <typename T, bool PB>
 hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
   const long long rows = (long long)p.batch * p.heads;
   if (rows >= 8LL * kNumCUs && p.heads % 8 == 0)
-    hipLaunchKernelGGL((merge_kernel<T, 8>), dim3(p.batch, p.heads / 8), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((merge_kernel<T, 8, PB>), dim3(p.batch, p.heads / 8), dim3(256), 0, s, p);
   else if (rows >= 4LL * kNumCUs && p.heads % 4 == 0)
-    hipLaunchKernelGGL((merge_kernel<T, 4>), dim3(p.batch, p.heads / 4), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((merge_kernel<T, 4, PB>), dim3(p.batch, p.heads / 4), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((merge_kernel<T, 2>), dim3(p.batch, p.heads / 2), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((merge_kernel<T, 2, PB>), dim3(p.batch, p.heads / 2), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, bool f32, hipStream_t s) {
+hipError_t launch_decode(const DecodeParams& params, bool f32, hipStream_t s) {
+  DecodeParams p = params;
   hipError_t e;
-  if (f32) {
+  if (f32) {  // debug mode: fp32 everywhere, fp32 pieces
+    p.partial_bf16 = 0;
     e = launch_valu<float>(p, s);
-    if (e == hipSuccess) e = launch_merge<float>(p, s);
+    if (e == hipSuccess) e = launch_merge<float, false>(p, s);
+  } else if (mfma_supported(p)) {  // the matrix-core kernel writes normalised bf16 pieces
+    p.partial_bf16 = 1;
+    e = launch_decode_mfma(p, s);
+    if (e == hipSuccess) {
+      if (p.num_units >= 16 * p.batch) {  // long sequences: many pieces each
+        hipLaunchKernelGGL(merge_pieces_kernel<uint16_t>, dim3(p.batch, p.heads), dim3(256), 0, s, p);
+        e = hipGetLastError();
+      } else {
+        e = launch_merge<uint16_t, true>(p, s);
+      }
+    }
   } else {
-    e = mfma_supported(p) ? launch_decode_mfma(p, s) : launch_valu<uint16_t>(p, s);
-    if (e == hipSuccess) e = launch_merge<uint16_t>(p, s);
+    p.partial_bf16 = 0;
+    e = launch_valu<uint16_t>(p, s);
+    if (e == hipSuccess) e = launch_merge<uint16_t, false>(p, s);
   }
   return e;
 }

@@ -303,6 +303,19 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   const unsigned v_off = (unsigned)(tile_offset(4 * half + ((lane & 15) >> 2),
                                                 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1));
 
+  // The query of a segment lives in VGPRs for the whole segment (36 x 8 bf16 per lane).
+  const uint16_t* qa = static_cast<const uint16_t*>(p.q_abs);
+  bf16x8 q[36];
+  auto load_q = [&](int b) __attribute__((always_inline)) {
+    const int ln = lane_id();
+    const uint16_t* qrow = qa + ((size_t)b * p.heads + wave * 32 + (ln & 31)) * kRow + 8 * (ln >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+  };
+  // The first segment's query is requested ahead of the first copies, so that waiting for it does
+  // not wait for them.
+  load_q(cp.b);
+
   // Prologue: three tiles in flight.
   int issued = 0;
 #pragma unroll
@@ -313,6 +326,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       ++issued;
     }
   }
+  // Loads complete in issue order: with at most the prologue's copies outstanding (capped at the
+  // counter's 63, which only waits for more), the query has landed.
+  if (issued >= 3) wait_vmcnt<(3 * kPer < 63 ? 3 * kPer : 63)>();
+  else if (issued == 2) wait_vmcnt<(2 * kPer < 63 ? 2 * kPer : 63)>();
+  else wait_vmcnt<(kPer < 63 ? kPer : 63)>();
   // Waits until the copies of tile `t` (this wave's part) have landed, then for every wave.
   // Vector loads complete in issue order: it is enough to let the tiles issued after it stay in
   // flight.
@@ -332,21 +350,18 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     }
   };
 
-  const uint16_t* qa = static_cast<const uint16_t*>(p.q_abs);
   const float scale = p.scale_log2;
   int it = 0;  // tile index within the unit
+  bool first_segment = true;
   while (cp.valid) {  // one segment: the part of sequence b inside this unit
     const int b = cp.b;
-    bf16x8 q[36];
-    {
-      const int ln = lane_id();
-      const uint16_t* qrow = qa + ((size_t)b * p.heads + wave * 32 + (ln & 31)) * kRow + 8 * (ln >> 5);
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+    if (!first_segment) {
+      load_q(b);
       // Wait here, once per segment: left to the compiler, the wait for Q would sit inside the tile
-      // loop and drain the DMA ring on every tile.
+      // loop and drain the copy ring on every tile.
       wait_vmcnt<0>();
     }
+    first_segment = false;
     f32x16 o[16];
     {
       const bf16x8 zero = {};
@@ -512,19 +527,23 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       ++it;
     } while (!last);
 
-    // ---- end of segment: the un-normalised sum leaves straight from the accumulators; the merge
-    // kernel divides by the softmax sum.
+    // ---- end of segment: the piece's sum, divided by its softmax sum, is stored in bf16 (half the
+    // bytes of the fp32 sum; the merge weighs it by that sum again) with (reference max, sum).
     const float l_tot = sum_halves(l_sum);
+    const float inv = 1.f / l_tot;
     mfma_a_drain(o);
     const int ln = lane_id();
     const size_t part = ((size_t)w + b) * p.heads + wave * 32 + (ln & 31);
-    float* orow = p.ws_o + part * kDc + 4 * (ln >> 5);
+    uint16_t* orow = reinterpret_cast<uint16_t*>(p.ws_o + part * kDc) + 4 * (ln >> 5);
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(orow + 32 * db + 8 * g) =
-            make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+      for (int g = 0; g < 4; ++g) {
+        uint2 packed;
+        packed.x = (uint32_t)f32_to_bf16(o[db][4 * g] * inv) | ((uint32_t)f32_to_bf16(o[db][4 * g + 1] * inv) << 16);
+        packed.y = (uint32_t)f32_to_bf16(o[db][4 * g + 2] * inv) | ((uint32_t)f32_to_bf16(o[db][4 * g + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * g) = packed;
+      }
     }
     if (ln < 32) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_ref, l_tot);
   }

@@ -125,6 +125,7 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
   p.heads = num_heads;
   p.num_units = units;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.partial_bf16 = 0;  // chosen with the kernel in launch_decode
   hipError_t e = launch_decode(p, dtype == MLA_F32, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -24,8 +24,10 @@ struct DecodeParams {
   const int32_t* seq_lens;
   void* o_lat;
   float* lse;          // may be null
-  float* ws_o;         // [units + batch][heads][512] fp32 un-normalised partial outputs
+  float* ws_o;         // [units + batch][heads][512] fp32 slots of the partial outputs
   float* ws_ml;        // [units + batch][heads][2] fp32 (base-2 reference max, softmax sum)
+  int partial_bf16;    // 0: fp32 un-normalised sums; 1: bf16 sums already divided by the
+                       // softmax sum, in the first half of each slot (set by launch_decode)
   int num_pages;
   int max_blocks;
   int batch;
