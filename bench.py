@@ -141,7 +141,7 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str):
             raise SystemExit(f"{counter}: no calibration copy found in {folder}")
         scale = CALIB_BYTES / calib
         total = 0.0
-        for tag in ("decode_mfma_kernel", "merge_kernel"):
+        for tag in ("decode_mfma_kernel", "merge"):
             vals = [float(r["Counter_Value"]) * 1024 for r in rows if tag in r["Kernel_Name"]]
             if not vals:
                 raise SystemExit(f"{counter}: no {tag} dispatch in {folder}")
