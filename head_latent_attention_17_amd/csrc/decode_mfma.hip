@@ -278,6 +278,14 @@ __device__ __forceinline__ bf16x8 v_operand(unsigned tv, int db, int m) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Workgroups go to the eight XCDs round-robin (workgroup i to XCD i mod 8), each XCD with its own
+// L2.  Consecutive work units, which hold neighbouring pages and mostly the same sequence, are
+// placed on one XCD so that they share its L2 for that sequence's query and block-table lines.
+__device__ __forceinline__ int xcd_unit(int id, int n) {
+  const int per = n / 8, rem = n % 8, x = id % 8;
+  return x * per + min(x, rem) + id / 8;
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p) {
   constexpr int kPer = kBlocks / NW;  // copies per wave per tile
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   const int half = lane >> 5;       // which K half of the MFMA operands this lane holds
   const int l32 = lane & 31;
   const int head = wave * 32 + l32; // head of this lane's score / output column
-  const int w = blockIdx.x;
+  const int w = uni(xcd_unit(blockIdx.x, gridDim.x));
 
   TileCursor ld, cp;
   ld.init(p, w);
