@@ -3,22 +3,22 @@
 //   out-proj: out[b][h][:]   = o_lat[b][h][:]  (512) @ W_UV[h] (512 x 128)
 // (DeepSeek-V2 explainer, Step 6: the query side absorbs W_UK, the output side applies W_UV after
 // the weighted sum.)  Both are C[b][n] = sum_k A[b][k] W[k][n] per head with M = batch; each weight
-// matrix is read from HBM once per launch and is the dominant traffic, so the kernel streams W
-// through LDS in 128-row chunks and applies every chunk to the whole batch.
+// matrix is read from HBM once per launch and is the dominant traffic, so each workgroup copies its
+// slice of W to LDS once and applies it to the whole batch.
 //
-// Work split: one workgroup per (head, 32 output columns), so every weight byte is fetched by
-// exactly one workgroup and a launch has heads x N / 32 workgroups (2048 for the absorption, 512
-// for the out-projection).  The workgroup's weight slab (K rows x 64 bytes) is copied HBM -> LDS
-// in one go with global_load_lds_dwordx4 (16 rows per copy, no registers held), while the batch
-// rows of A are fetched straight into registers.  The four waves split K (wave w takes k-steps
-// w, w + 4, ...) and their partial 32 x 32 tiles are summed through LDS.
+// Work split: one workgroup per (head, 32 NB output columns), so every weight byte is fetched by
+// exactly one workgroup (with NB = 1: 2,048 workgroups for the absorption, 512 for the
+// out-projection).  The workgroup's weight slab (K rows x 64 NB bytes) is copied HBM -> LDS in one
+// go with global_load_lds_dwordx4 (1 KB per copy, no registers held), while the batch rows of A are
+// fetched straight into registers.  The four waves split the column blocks and K; partial tiles of
+// one column block are summed through LDS.
 //
 // Operands of v_mfma_f32_32x32x16_bf16: A (32 batch rows x 16 k) is 8 consecutive k of one row per
 // lane, read from global memory; B (16 k x 32 columns) needs 8 consecutive k of one column per
 // lane while W is stored with columns contiguous, so it comes out of the LDS slab with two 16-lane
 // transposing reads (ds_read_b64_tr_b16), each giving a lane 4 consecutive rows of its column.
-// Slab rows are 64 bytes, so the 4 rows x 32 bytes of one 16-lane read cover 256 consecutive
-// bytes: no bank conflicts.
+// With 64-byte slab rows the 4 rows x 32 bytes of one 16-lane read cover 256 consecutive bytes: no
+// bank conflicts; wider rows are swizzled to the same effect.
 #include "mla_device.h"
 
 namespace mla {
@@ -42,31 +42,48 @@ __device__ __forceinline__ void dma16(const void* gaddr, unsigned lds) {
                : "memory", "m0");
 }
 
-// MB = 32-row batch blocks per pass.
-template <int K, int N, int MB>
+// MB = 32-row batch blocks per pass; NB = 32-column blocks per workgroup.  The four waves are NB
+// column blocks x (4 / NB) slices of K; with more than one slice their partial tiles are summed
+// through LDS.  A slab row is 64 NB bytes; for NB > 1 the 16-byte units of row r are stored XOR
+// g(r) = 2 ((r 64 NB / 256) mod 4) so that the four rows of one transposing read fall on different
+// banks.
+template <int NB>
+__device__ __forceinline__ int slab_swz(int r) {
+  constexpr int U = 4 * NB;  // 16-byte units per slab row
+  return NB == 1 ? 0 : ((2 * ((r * U / 16) & 3)) & (U - 1));
+}
+
+template <int K, int N, int MB, int NB>
 __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restrict__ a, int lda,
                                                         const uint16_t* __restrict__ w,
                                                         uint16_t* __restrict__ c, int ldc,
                                                         int batch, int heads) {
+  constexpr int KS = 4 / NB;            // K slices
+  constexpr int RB = 64 * NB;           // slab row bytes
+  constexpr int U = RB / 16;            // 16-byte units per slab row
   constexpr int kSteps = K / 16;        // k-steps of the product
-  constexpr int kPerWave = kSteps / 4;  // k-steps per wave
-  __shared__ __attribute__((aligned(1024))) char slab[K * 64];
-  __shared__ __attribute__((aligned(16))) float red[4][32 * 32];
+  constexpr int kPerWave = kSteps / KS; // k-steps per wave
+  constexpr int kCopies = K * RB / 1024;
+  __shared__ __attribute__((aligned(1024))) char slab[K * RB];
+  __shared__ __attribute__((aligned(16))) float red[KS > 1 ? 4 : 1][32 * 32];
   const int h = blockIdx.x;
-  const int n0 = blockIdx.y * kNT;
+  const int n0 = blockIdx.y * kNT * NB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
+  const int cb = wave % NB;             // column block of this wave
+  const int ksl = wave / NB;            // K slice of this wave
 
-  // Weight slab: copy j of this wave moves rows 16 (4 j + wave) .. + 15, 64 bytes each.
+  // Weight slab: copy i moves 1024 / RB rows; lane l fetches unit (l % U) ^ g(row) of row l / U.
   {
     const uint16_t* wh = w + (size_t)h * K * N + n0;
     const unsigned lds0 = (unsigned)(uintptr_t)(LDS_AS char*)slab;
 #pragma unroll
-    for (int j = 0; j < K / 64; ++j) {
-      const int r0 = 16 * (4 * j + wave);
-      dma16(wh + (size_t)(r0 + (lane >> 2)) * N + 8 * (lane & 3), lds0 + r0 * 64);
+    for (int i = wave; i < kCopies; i += 4) {
+      const int r = i * (1024 / RB) + lane / U;
+      const int u = (lane % U) ^ slab_swz<NB>(r);
+      dma16(wh + (size_t)r * N + 8 * u, lds0 + i * 1024);
     }
   }
   if (K == kDnope && blockIdx.y == 0) {
@@ -78,10 +95,16 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
     }
   }
 
-  // Transposing-read address of this lane (row within a k-step, byte within a row): rows
-  // 8 half + (lane % 16) / 4 (+ 4 for the second read), columns 16 ((lane / 16) % 2) + 4 (lane % 4).
-  const unsigned tr_off = (unsigned)(uintptr_t)(LDS_AS char*)slab +
-                          (8 * half + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  // Transposing reads: row 8 half + (lane % 16) / 4 of a k-step (+ 4 for the second read), logical
+  // unit 4 cb + 2 ((lane / 16) % 2) + (lane % 4) / 2, byte 8 (lane % 2).  g(row) repeats every 16
+  // rows, so a k-step is an immediate offset.
+  unsigned tr_off[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int r = 8 * half + ((lane & 15) >> 2) + 4 * rd;
+    const int u = 4 * cb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tr_off[rd] = (unsigned)(uintptr_t)(LDS_AS char*)slab + r * RB + 16 * (u ^ slab_swz<NB>(r)) + 8 * (lane & 1);
+  }
 
   for (int m0 = 0; m0 < batch; m0 += 32 * MB) {
     f32x16 acc[MB];
@@ -92,7 +115,7 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
       const int row = m0 + 32 * mb + (lane & 31);
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) {
-        const int ks = wave + 4 * i;
+        const int ks = ksl + KS * i;
         aop[mb][i] = bf16x8{};
         if (row < batch)
           aop[mb][i] = *reinterpret_cast<const bf16x8*>(a + ((size_t)row * heads + h) * lda + 16 * ks + 8 * half);
@@ -104,68 +127,89 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
     }
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int ks = wave + 4 * i;
-      const LDS_AS char* p0 = (const LDS_AS char*)(uintptr_t)tr_off + ks * 16 * 64;
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p0);
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p0 + 4 * 64));
+      const int ks = ksl + KS * i;
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)((LDS_AS char*)(uintptr_t)tr_off[0] + ks * 16 * RB));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)((LDS_AS char*)(uintptr_t)tr_off[1] + ks * 16 * RB));
       const bf16x8 bop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[mb][i], bop, acc[mb], 0, 0, 0);
     }
-    // Sum the four waves' partial tiles: acc lane l, register j is row 8 (j / 4) + 4 half + j % 4,
-    // column l % 32.  Thread t then owns row t / 8, columns 4 (t % 8) .. + 3.
+    // acc lane l, register j is row 8 (j / 4) + 4 half + j % 4, column l % 32 of this wave's block.
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (m0 + 32 * mb >= batch) break;
+      if constexpr (KS == 1) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        red[wave][(8 * (j >> 2) + 4 * half + (j & 3)) * 32 + (lane & 31)] = acc[mb][j];
-      __syncthreads();
-      const int r = tid >> 3, c4 = 4 * (tid & 7);
-      float4 sum = *reinterpret_cast<const float4*>(&red[0][r * 32 + c4]);
+        for (int j = 0; j < 16; ++j) {
+          const int row = m0 + 32 * mb + 8 * (j >> 2) + 4 * half + (j & 3);
+          if (row < batch) c[((size_t)row * heads + h) * ldc + n0 + 32 * cb + (lane & 31)] = f32_to_bf16(acc[mb][j]);
+        }
+      } else {
+        // Sum the K slices through LDS: thread t then owns row t / 8 of column block (t / 8) ..
 #pragma unroll
-      for (int q = 1; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(&red[q][r * 32 + c4]);
-        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+        for (int j = 0; j < 16; ++j)
+          red[wave][(8 * (j >> 2) + 4 * half + (j & 3)) * 32 + (lane & 31)] = acc[mb][j];
+        __syncthreads();
+        // 32 x 32 NB outputs, 256 threads: thread t covers column block t % NB, row (t / NB) % 32,
+        // columns 4 ((t / (32 NB)) ..) in steps; done as NB x 32 rows x 8 groups of 4 columns.
+#pragma unroll
+        for (int e = tid; e < NB * 32 * 8; e += 256) {
+          const int blk = e / (32 * 8), r = (e / 8) % 32, c4 = 4 * (e % 8);
+          float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int q = 0; q < KS; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(&red[q * NB + blk][r * 32 + c4]);
+            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+          }
+          const int row = m0 + 32 * mb + r;
+          if (row < batch) {
+            uint2 packed;
+            packed.x = (uint32_t)f32_to_bf16(sum.x) | ((uint32_t)f32_to_bf16(sum.y) << 16);
+            packed.y = (uint32_t)f32_to_bf16(sum.z) | ((uint32_t)f32_to_bf16(sum.w) << 16);
+            *reinterpret_cast<uint2*>(c + ((size_t)row * heads + h) * ldc + n0 + 32 * blk + c4) = packed;
+          }
+        }
+        __syncthreads();
       }
-      const int row = m0 + 32 * mb + r;
-      if (row < batch) {
-        uint2 packed;
-        packed.x = (uint32_t)f32_to_bf16(sum.x) | ((uint32_t)f32_to_bf16(sum.y) << 16);
-        packed.y = (uint32_t)f32_to_bf16(sum.z) | ((uint32_t)f32_to_bf16(sum.w) << 16);
-        *reinterpret_cast<uint2*>(c + ((size_t)row * heads + h) * ldc + n0 + c4) = packed;
-      }
-      __syncthreads();
     }
   }
 }
 
-template <int K, int N>
+// Column blocks per workgroup.  Measured on the MI355X at batch 32 to 128: one block (2,048 and 512
+// workgroups, four K slices) is as fast as or faster than two or four (fewer workgroups, larger slabs).
+#ifndef MLA_NB_ABSORB
+#define MLA_NB_ABSORB 1
+#endif
+#ifndef MLA_NB_OUT
+#define MLA_NB_OUT 1
+#endif
+
+template <int K, int N, int NB>
 void launch_gemm(const void* a, int lda, const void* w, void* c, int ldc, int batch, int heads, hipStream_t s) {
-  const dim3 grid(heads, N / kNT);
+  const dim3 grid(heads, N / (kNT * NB));
   const uint16_t* A = (const uint16_t*)a;
   const uint16_t* W = (const uint16_t*)w;
   uint16_t* C = (uint16_t*)c;
   if (batch <= 32)
-    hipLaunchKernelGGL((head_gemm_kernel<K, N, 1>), grid, dim3(256), 0, s, A, lda, W, C, ldc, batch, heads);
+    hipLaunchKernelGGL((head_gemm_kernel<K, N, 1, NB>), grid, dim3(256), 0, s, A, lda, W, C, ldc, batch, heads);
   else if (batch <= 64)
-    hipLaunchKernelGGL((head_gemm_kernel<K, N, 2>), grid, dim3(256), 0, s, A, lda, W, C, ldc, batch, heads);
+    hipLaunchKernelGGL((head_gemm_kernel<K, N, 2, NB>), grid, dim3(256), 0, s, A, lda, W, C, ldc, batch, heads);
   else
-    hipLaunchKernelGGL((head_gemm_kernel<K, N, 4>), grid, dim3(256), 0, s, A, lda, W, C, ldc, batch, heads);
+    hipLaunchKernelGGL((head_gemm_kernel<K, N, 4, NB>), grid, dim3(256), 0, s, A, lda, W, C, ldc, batch, heads);
 }
 
 }  // namespace
 
 hipError_t launch_absorb_mfma(const void* q, const void* w_uk, void* q_abs, int batch, int heads,
                               hipStream_t s) {
-  launch_gemm<kDnope, kDc>(q, kQdim, w_uk, q_abs, kRow, batch, heads, s);
+  launch_gemm<kDnope, kDc, MLA_NB_ABSORB>(q, kQdim, w_uk, q_abs, kRow, batch, heads, s);
   return hipGetLastError();
 }
 
 hipError_t launch_out_proj_mfma(const void* o_lat, const void* w_uv, void* out, int batch, int heads,
                                 hipStream_t s) {
-  launch_gemm<kDc, kDv>(o_lat, kDc, w_uv, out, kDv, batch, heads, s);
+  launch_gemm<kDc, kDv, MLA_NB_OUT>(o_lat, kDc, w_uv, out, kDv, batch, heads, s);
   return hipGetLastError();
 }
 
