@@ -290,6 +290,9 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p) {
   constexpr int kPer = kBlocks / NW;  // copies per wave per tile
   __shared__ __attribute__((aligned(1024))) char ring[kStages][kTileBytes];
+  // Target of the copies a four-wave unit issues after its last tile: they keep the count of copies
+  // per tile fixed, which the counted waits rely on, and nothing reads them.
+  __shared__ __attribute__((aligned(1024))) char sink[NW == 4 ? kPer * 1024 : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -405,7 +408,36 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // The next tile must be in LDS before its scores start; the barrier also frees the stage of
       // tile it - 1, which is refilled at once.
       tile_ready(last ? it : it + 1);
-      refill(it);
+      // Copies of tile it + 3 into the stage of tile it - 1.  With four waves, each wave copies one
+      // token group (nine 1 KB blocks), one block per four score MFMAs below: 36 copies at once
+      // would queue in the address unit and hold every wave for hundreds of cycles.  A ragged tile
+      // repeats its last row in place of the missing ones; after the unit's last tile the copies
+      // go to the sink (from the first page, which always exists).
+      const char* sp_base = nullptr;
+      unsigned sp_lane = 0, sp_lds = 0;
+      if constexpr (NW == 4) {
+        const int ln = lane_id();
+        const int tl = (ln >> 3) ^ (wave & 1);
+        const unsigned cl16 = (unsigned)((ln & 7) ^ sigma(tl)) * 16u;
+        if (ld.valid) {
+          const int page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + ld.t / kPage);
+          const int ntl = min(kTileTok, ld.t_end - ld.t);
+          sp_base = reinterpret_cast<const char*>(p.cache) + ((size_t)page * kPage + (ld.t % kPage)) * (kRow * 2);
+          sp_lane = (unsigned)min(8 * wave + tl, ntl - 1) * (kRow * 2) + cl16;
+          sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)ring[(it + kStages - 1) % kStages] + wave * kPer * 1024;
+          ld.advance();
+        } else {
+          sp_base = reinterpret_cast<const char*>(p.cache);
+          sp_lane = (unsigned)(8 * wave + tl) * (kRow * 2) + cl16;
+          sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)sink;
+        }
+        ++issued;
+      } else {
+        refill(it);
+      }
+      auto spread_copy = [&](int j) __attribute__((always_inline)) {
+        if constexpr (NW == 4) dma16(sp_base + j * 128, sp_lane, sp_lds + j * 1024);
+      };
 
       // ---- softmax of tile it (base 2), lane = head, registers = tokens, spread over the next
       // tile's score MFMAs -------------------------------------------------------------------------
@@ -466,12 +498,15 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
           if (ks + kKAhead < 36) ka[(ks + kKAhead) % (kKAhead + 1)] = k_operand(tk, ks + kKAhead);
           if (ks == 0) mfma_v_first_nw(s_nxt, ka[0], q[0]); else mfma_v_nw(s_nxt, ka[ks % (kKAhead + 1)], q[ks]);
           softmax_step(ks);
+          if ((ks & 3) == 0) spread_copy(ks >> 2);
           __builtin_amdgcn_sched_barrier(0);
         }
         mfma_v_drain(s_nxt);
       } else {
 #pragma unroll
         for (int k = 0; k < 13; ++k) softmax_step(k);
+#pragma unroll
+        for (int j = 0; j < kCG; ++j) spread_copy(j);
       }
 
       if (__builtin_expect(rescale, 0)) {
@@ -555,6 +590,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     }
     if (ln < 32) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_ref, l_tot);
   }
+  // No copy into LDS may still be in flight when the workgroup ends.
+  wait_vmcnt<0>();
 }
 
 }  // namespace
