@@ -38,6 +38,9 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 #define LDS_AS __attribute__((address_space(3)))
 #define CONST_AS __attribute__((address_space(4)))
 
@@ -577,15 +580,43 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     mfma_a_drain(o);
     const int ln = lane_id();
     const size_t part = ((size_t)w + b) * p.heads + wave * 32 + (ln & 31);
-    uint16_t* orow = reinterpret_cast<uint16_t*>(p.ws_o + part * kDc) + 4 * (ln >> 5);
+    // four sums of one lane, divided by the softmax sum, rounded to bf16 (nearest even)
+    auto packed_out = [&](int db, int g) __attribute__((always_inline)) {
+      const bf16x4 v = {(__bf16)(o[db][4 * g] * inv), (__bf16)(o[db][4 * g + 1] * inv),
+                        (__bf16)(o[db][4 * g + 2] * inv), (__bf16)(o[db][4 * g + 3] * inv)};
+      return __builtin_bit_cast(u32x2, v);
+    };
+    if constexpr (NW == 4) {
+      // Rows go through LDS and leave as 256-byte quarter rows instead of 16-byte pieces of 32
+      // rows per store.  Once every wave is done with the last tile its stage is free: each wave
+      // takes a quarter of it, 32 heads x 128 dims padded by 16 bytes per row against bank
+      // conflicts, and passes its rows through it a quarter at a time.
+      constexpr int kPad = 256 + 16;
+      __builtin_amdgcn_s_barrier();
+      LDS_AS char* region = (LDS_AS char*)ring[(it - 1) % kStages] + wave * 32 * kPad;
+      const int hw = ln & 31, hl = ln >> 5;
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
+      for (int qt = 0; qt < 4; ++qt) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 packed;
-        packed.x = (uint32_t)f32_to_bf16(o[db][4 * g] * inv) | ((uint32_t)f32_to_bf16(o[db][4 * g + 1] * inv) << 16);
-        packed.y = (uint32_t)f32_to_bf16(o[db][4 * g + 2] * inv) | ((uint32_t)f32_to_bf16(o[db][4 * g + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * g) = packed;
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<LDS_AS u32x2*>(region + hw * kPad + (32 * d + 8 * g + 4 * hl) * 2) = packed_out(4 * qt + d, g);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int h = 4 * k + (ln >> 4);
+          const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(region + h * kPad + (ln & 15) * 16);
+          const size_t ph = ((size_t)w + b) * p.heads + wave * 32 + h;
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.ws_o + ph * kDc) + 128 * qt + 8 * (ln & 15)) = v;
+        }
+      }
+    } else {
+      uint16_t* orow = reinterpret_cast<uint16_t*>(p.ws_o + part * kDc) + 4 * (ln >> 5);
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g) = packed_out(db, g);
       }
     }
     if (ln < 32) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_ref, l_tot);
