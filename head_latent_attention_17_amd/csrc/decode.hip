@@ -131,6 +131,52 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   }
 }
 
+// Units that hold sequence b: [wf, wl], from the table the matrix-core kernel writes, else derived
+// from seq_lens.  A unit in that range holds no page (and wrote nothing) only when there are more
+// units than pages.
+struct SeqUnits {
+  int wf, wl, W;
+  bool all_live;
+  long long P;
+  __device__ __forceinline__ bool live(int w) const {
+    return all_live || unit_start(P, W, w) != unit_start(P, W, w + 1);
+  }
+};
+
+__device__ __forceinline__ SeqUnits seq_units_of(const DecodeParams& p, int b, long long np) {
+  SeqUnits u;
+  u.W = p.num_units;
+  u.P = 0;
+  if (p.seq_units) {
+    const int4 d = *reinterpret_cast<const int4*>(p.seq_units + 4 * b);
+    u.wf = d.x;
+    u.wl = d.y;
+    u.all_live = d.z != 0;
+    if (!u.all_live) u.P = total_pages(p.seq_lens, p.batch);
+  } else {
+    u.P = total_pages(p.seq_lens, p.batch);
+    const long long before = pages_before(p.seq_lens, b);
+    u.wf = unit_of_page(u.P, u.W, before);
+    u.wl = unit_of_page(u.P, u.W, before + np - 1);
+    u.all_live = u.P >= u.W;
+  }
+  return u;
+}
+
+// Eight consecutive outputs from one lane (one 16-byte store for bf16, two for fp32).
+__device__ __forceinline__ void store8(uint16_t* o, size_t i, const float* x) {
+  uint4 v;
+  v.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+  v.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+  v.z = (uint32_t)f32_to_bf16(x[4]) | ((uint32_t)f32_to_bf16(x[5]) << 16);
+  v.w = (uint32_t)f32_to_bf16(x[6]) | ((uint32_t)f32_to_bf16(x[7]) << 16);
+  *reinterpret_cast<uint4*>(o + i) = v;
+}
+__device__ __forceinline__ void store8(float* o, size_t i, const float* x) {
+  *reinterpret_cast<float4*>(o + i) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(o + i + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+
 // Finishes every sequence: combines its pieces (one per work unit it touches, stored at slot
 // unit + sequence), divides by the softmax sum and writes o_lat and lse.
 //   M = max_s m_s;  w_s = 2^(m_s - M);  o = sum_s w_s O_s / sum_s w_s l_s;  lse = ln2 (M + log2 sum_s w_s l_s)
@@ -160,14 +206,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     if (p.lse && j == 0) p.lse[(size_t)b * p.heads + h] = -INFINITY;
     return;
   }
-  const long long P = total_pages(p.seq_lens, p.batch);
-  const long long before = pages_before(p.seq_lens, b);
-  const int W = p.num_units;
-  const int wf = unit_of_page(P, W, before);
-  const int wl = unit_of_page(P, W, before + np - 1);
-  // Units that hold no page (possible only when there are more units than pages) wrote nothing.
-  const bool all_live = P >= W;
-  auto live = [&](int w) { return all_live || unit_start(P, W, w) != unit_start(P, W, w + 1); };
+  const SeqUnits su = seq_units_of(p, b, np);
+  const int wf = su.wf, wl = su.wl;
+  auto live = [&](int w) { return su.live(w); };
   auto slot = [&](int w) { return ((size_t)w + b) * p.heads + h; };
 
   float mx = -INFINITY;
@@ -270,13 +311,9 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(DecodeParams p) {
     }
     return;
   }
-  const long long P = total_pages(p.seq_lens, p.batch);
-  const long long before = pages_before(p.seq_lens, b);
-  const int W = p.num_units;
-  const int wf = unit_of_page(P, W, before);
-  const int wl = unit_of_page(P, W, before + np - 1);
-  const bool all_live = P >= W;
-  auto live = [&](int w) { return all_live || unit_start(P, W, w) != unit_start(P, W, w + 1); };
+  const SeqUnits su = seq_units_of(p, b, np);
+  const int wf = su.wf, wl = su.wl;
+  auto live = [&](int w) { return su.live(w); };
   auto slot = [&](int w) { return ((size_t)w + b) * p.heads + h; };
 
   float mx = -INFINITY, sum = 0.f;
@@ -341,13 +378,15 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(DecodeParams p) {
       tot += wq[q] * red_ms[q][1];
     }
     const float inv = 1.f / tot;
+    float x[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float x = 0.f;
+      x[i] = 0.f;
 #pragma unroll
-      for (int q = 0; q < kGroups; ++q) x = fmaf(wq[q], red_acc[q][8 * l + i], x);
-      Elem<OT>::store(o, ob + 8 * l + i, x * inv);
+      for (int q = 0; q < kGroups; ++q) x[i] = fmaf(wq[q], red_acc[q][8 * l + i], x[i]);
+      x[i] *= inv;
     }
+    store8(o, ob + 8 * l, x);
     if (p.lse && l == 0) p.lse[(size_t)b * p.heads + h] = (M + log2f(tot)) * 0.69314718055994531f;
   }
 }
@@ -372,6 +411,7 @@ hipError_t launch_decode(const DecodeParams& params, bool f32, hipStream_t s) {
   hipError_t e;
   if (f32) {  // debug mode: fp32 everywhere, fp32 pieces
     p.partial_bf16 = 0;
+    p.seq_units = nullptr;
     e = launch_valu<float>(p, s);
     if (e == hipSuccess) e = launch_merge<float, false>(p, s);
   } else if (mfma_supported(p)) {  // the matrix-core kernel writes normalised bf16 pieces
@@ -387,6 +427,7 @@ hipError_t launch_decode(const DecodeParams& params, bool f32, hipStream_t s) {
     }
   } else {
     p.partial_bf16 = 0;
+    p.seq_units = nullptr;
     e = launch_valu<uint16_t>(p, s);
     if (e == hipSuccess) e = launch_merge<uint16_t, false>(p, s);
   }

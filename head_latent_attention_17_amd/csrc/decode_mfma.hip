@@ -158,6 +158,7 @@ struct TileCursor {
   int t;          // first token of the current tile
   int t_end;      // end token of the current segment
   bool valid;
+  bool all_live;  // every unit holds at least one page
 
   __device__ __forceinline__ void load_seq() {
     len = ld_const(lens, b);
@@ -179,6 +180,7 @@ struct TileCursor {
     const int P = uni((int)total_pages(p.seq_lens, p.batch));
     pg0 = uni((int)((long long)w * P / p.num_units));
     pg1 = uni((int)((long long)(w + 1) * P / p.num_units));
+    all_live = P >= p.num_units;
     valid = pg0 < pg1;
     if (!valid) return;
     int bb;
@@ -369,6 +371,13 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   bool first_segment = true;
   while (cp.valid) {  // one segment: the part of sequence b inside this unit
     const int b = cp.b;
+    if (threadIdx.x == 0) {  // the merge reads the range of units that hold sequence b from here
+      if (cp.t == 0) {
+        p.seq_units[4 * b] = w;
+        p.seq_units[4 * b + 2] = cp.all_live ? 1 : 0;
+      }
+      if (cp.t_end == cp.len) p.seq_units[4 * b + 1] = w;
+    }
     if (!first_segment) {
       load_q(b);
       // Wait here, once per segment: left to the compiler, the wait for Q would sit inside the tile

@@ -18,10 +18,11 @@ int auto_units(int batch, int heads, int max_blocks) {
 }
 
 // One partial result per (unit, sequence) piece.  Pieces are numbered unit + sequence, which grows
-// strictly along the page order, so units + batch slots always suffice.
+// strictly along the page order, so units + batch slots always suffice.  Then 16 bytes per sequence
+// for the range of units that hold it.
 size_t workspace_bytes(int batch, int heads, int units) {
   const size_t parts = ((size_t)units + (size_t)batch) * (size_t)heads;
-  return parts * (size_t)kDc * sizeof(float) + parts * 2 * sizeof(float);
+  return parts * (size_t)kDc * sizeof(float) + parts * 2 * sizeof(float) + (size_t)batch * 4 * sizeof(int);
 }
 
 }  // namespace mla
@@ -119,6 +120,7 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
   p.lse = lse;
   p.ws_o = static_cast<float*>(workspace);
   p.ws_ml = p.ws_o + ((size_t)units + batch) * num_heads * kDc;
+  p.seq_units = reinterpret_cast<int*>(p.ws_ml + ((size_t)units + batch) * num_heads * 2);
   p.num_pages = num_pages;
   p.max_blocks = max_blocks_per_seq;
   p.batch = batch;

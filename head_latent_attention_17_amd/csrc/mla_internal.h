@@ -26,6 +26,9 @@ struct DecodeParams {
   float* lse;          // may be null
   float* ws_o;         // [units + batch][heads][512] fp32 slots of the partial outputs
   float* ws_ml;        // [units + batch][heads][2] fp32 (base-2 reference max, softmax sum)
+  int* seq_units;      // [batch][4]: first unit, last unit, every unit holds a page (1 / 0), unused;
+                       // written by the matrix-core kernel, which sets it (null: the merges
+                       // derive the unit range from seq_lens)
   int partial_bf16;    // 0: fp32 un-normalised sums; 1: bf16 sums already divided by the
                        // softmax sum, in the first half of each slot (set by launch_decode)
   int num_pages;

@@ -46,9 +46,10 @@ def test_status_strings_and_version():
 def test_workspace_size_formula():
     L = _lib()
     # (units + batch) pieces * heads * (512 partial outputs + max + sum) * 4 bytes
-    assert L.mla_decode_workspace_size(4, 128, 2048, 64) == (64 + 4) * 128 * 514 * 4
-    assert L.mla_decode_workspace_size(4, 128, 2048, 0) == (256 + 4) * 128 * 514 * 4
-    assert L.mla_decode_workspace_size(1, 16, 3, 0) == (3 + 1) * 16 * 514 * 4   # never more units than pages
+    # one fp32 slot of 512 + 2 values per (piece, head), then 16 bytes per sequence
+    assert L.mla_decode_workspace_size(4, 128, 2048, 64) == (64 + 4) * 128 * 514 * 4 + 4 * 16
+    assert L.mla_decode_workspace_size(4, 128, 2048, 0) == (256 + 4) * 128 * 514 * 4 + 4 * 16
+    assert L.mla_decode_workspace_size(1, 16, 3, 0) == (3 + 1) * 16 * 514 * 4 + 16   # never more units than pages
     assert L.mla_decode_workspace_size(4, 100, 2048, 0) == 0                  # unsupported heads
     assert L.mla_decode_workspace_size(4, 128, 0, 0) == 0
     assert L.mla_decode_workspace_size(4, 128, 8, -1) == 0
