@@ -50,6 +50,8 @@ constexpr int kCG = kChunks / 8;                     // 9 chunk groups
 constexpr int kBlocks = kTileTok / 8 * kCG;          // 36 blocks of 8 tokens x 8 chunks
 constexpr int kTileBytes = kBlocks * 1024;           // 36,864
 constexpr int kStages = 4;                           // tiles it .. it+3
+static_assert((kStages & (kStages - 1)) == 0, "stage index by mask");
+__device__ __forceinline__ int stage_of(int t) { return t & (kStages - 1); }  // stage of tile t
 constexpr float kRescaleThreshold = 8.0f;            // base-2 headroom before O is rescaled
 #ifndef MLA_KAHEAD
 #define MLA_KAHEAD 3
@@ -137,10 +139,23 @@ __device__ __forceinline__ int ld_const(const int32_t* ptr, size_t i) {
   return ((const CONST_AS int32_t*)ptr)[i];
 }
 
+// Maxima of scores (finite or -inf) as single instructions: fmaxf would first quiet possible
+// signalling NaNs of every operand it cannot prove canonical, one extra instruction each.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // max / sum of a value and its copy in lane l ^ 32
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -218,6 +233,23 @@ __device__ __forceinline__ void dma16(const char* gbase, unsigned voff, unsigned
                : "memory", "m0");
 }
 
+// Copy j of a wave's token group: lane l's 16 bytes from gbase + voff + 128 j land at LDS byte
+// lds + 1024 j + 16 l.  The instruction offset (128 j) is added to the LDS address as well, so M0
+// takes lds + 896 j: one scalar add per copy.  j must fold to a constant.
+__device__ __forceinline__ void dma16_group(const char* gbase, unsigned voff, unsigned lds, int j) {
+  if (j == 0) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(gbase), "s"(lds)
+                 : "memory", "m0");
+  } else {
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%4"
+                 :
+                 : "v"(voff), "s"(gbase), "s"(lds), "i"(896 * j), "i"(128 * j)
+                 : "memory", "m0", "scc");
+  }
+}
+
 // DMA of one tile: wave w fills blocks [w * per, (w + 1) * per).  For a full tile the per-lane part
 // of every source address is one of two lane constants (token-group parity); a ragged tile (fewer
 // than 32 tokens) re-reads its last valid row in place of the missing ones.
@@ -241,11 +273,17 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, const TileCurs
       const int tl = (ln >> 3) ^ par;
       lane_off[par] = tl * (kRow * 2) + ((ln & 7) ^ sigma(tl)) * 16;
     }
+    if constexpr (NW == 4) {  // wave w copies token group w
+      const char* gb = base + wave * 8 * (kRow * 2);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int blk = wave * kPer + j;
-      const int tg = blk / kCG, cg = blk % kCG;
-      dma16(base + tg * 8 * (kRow * 2) + cg * 128, (unsigned)lane_off[tg & 1], lds + blk * 1024);
+      for (int j = 0; j < kPer; ++j) dma16_group(gb, (unsigned)lane_off[wave & 1], lds + wave * kPer * 1024, j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int blk = wave * kPer + j;
+        const int tg = blk / kCG, cg = blk % kCG;
+        dma16(base + tg * 8 * (kRow * 2) + cg * 128, (unsigned)lane_off[tg & 1], lds + blk * 1024);
+      }
     }
   } else {
 #pragma unroll
@@ -360,7 +398,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   // Refills the stage of the tile before `t` (every wave is past it) with the next tile.
   auto refill = [&](int t) __attribute__((always_inline)) {
     if (ld.valid) {
-      issue_tile<NW>(p, ld, (LDS_AS char*)ring[(t + kStages - 1) % kStages], wave);
+      issue_tile<NW>(p, ld, (LDS_AS char*)ring[stage_of(t + kStages - 1)], wave);
       ld.advance();
       ++issued;
     }
@@ -399,7 +437,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     f32x16 s_cur;
     {
       tile_ready(it);
-      const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[it % kStages] + k_off;
+      const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it)] + k_off;
       bf16x8 ka[kKAhead + 1];
 #pragma unroll
       for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tk, ks);
@@ -436,7 +474,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
           const int ntl = min(kTileTok, ld.t_end - ld.t);
           sp_base = reinterpret_cast<const char*>(p.cache) + ((size_t)page * kPage + (ld.t % kPage)) * (kRow * 2);
           sp_lane = (unsigned)min(8 * wave + tl, ntl - 1) * (kRow * 2) + cl16;
-          sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)ring[(it + kStages - 1) % kStages] + wave * kPer * 1024;
+          sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it + kStages - 1)] + wave * kPer * 1024;
           ld.advance();
         } else {
           sp_base = reinterpret_cast<const char*>(p.cache);
@@ -448,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         refill(it);
       }
       auto spread_copy = [&](int j) __attribute__((always_inline)) {
-        if constexpr (NW == 4) dma16(sp_base + j * 128, sp_lane, sp_lds + j * 1024);
+        if constexpr (NW == 4) dma16_group(sp_base, sp_lane, sp_lds, j);
       };
 
       // ---- softmax of tile it (base 2), lane = head, registers = tokens, spread over the next
@@ -473,11 +511,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
             }
           }
         } else if (k == 1) {
-          mt = fmaxf(fmaxf(fmaxf(s_cur[0], s_cur[1]), fmaxf(s_cur[2], s_cur[3])),
-                     fmaxf(fmaxf(s_cur[4], s_cur[5]), fmaxf(s_cur[6], s_cur[7])));
+          mt = max3(max3(s_cur[0], s_cur[1], s_cur[2]), max3(s_cur[3], s_cur[4], s_cur[5]),
+                    max2(s_cur[6], s_cur[7]));
         } else if (k == 2) {
-          mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(s_cur[8], s_cur[9]), fmaxf(s_cur[10], s_cur[11])),
-                               fmaxf(fmaxf(s_cur[12], s_cur[13]), fmaxf(s_cur[14], s_cur[15]))));
+          mt = max3(max3(mt, s_cur[8], s_cur[9]), max3(s_cur[10], s_cur[11], s_cur[12]),
+                    max3(s_cur[13], s_cur[14], s_cur[15]));
         } else if (k == 3) {
           mt = max_halves(mt) * scale;
         } else if (k == 4) {
@@ -501,7 +539,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       f32x16 s_nxt;
       if (!last) {
         // scores of tile it + 1 into s_nxt, one softmax step of tile it after each MFMA
-        const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[(it + 1) % kStages] + k_off;
+        const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it + 1)] + k_off;
         bf16x8 ka[kKAhead + 1];
 #pragma unroll
         for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tk, ks);
@@ -561,7 +599,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // then those of pb1 (the exponents of pb1 are computed during the first pass); operands
       // kVAhead MFMAs ahead.
       {
-        const unsigned tv = (unsigned)(uintptr_t)(LDS_AS char*)ring[it % kStages] + v_off;
+        const unsigned tv = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it)] + v_off;
         bf16x8 va[kVAhead + 1];
 #pragma unroll
         for (int i = 0; i < kVAhead; ++i) va[i] = v_operand(tv, i & 15, i >> 4);
@@ -602,7 +640,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // conflicts, and passes its rows through it a quarter at a time.
       constexpr int kPad = 256 + 16;
       __builtin_amdgcn_s_barrier();
-      LDS_AS char* region = (LDS_AS char*)ring[(it - 1) % kStages] + wave * 32 * kPad;
+      LDS_AS char* region = (LDS_AS char*)ring[stage_of(it - 1)] + wave * 32 * kPad;
       const int hw = ln & 31, hl = ln >> 5;
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
