@@ -404,6 +404,16 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     }
   };
 
+  // Scores of a ragged tile (n < 32 tokens) with the tokens past the end at -inf, so that they take
+  // no weight.  Lane half h, register j holds token 8 (j / 4) + 4 h + j % 4.
+  auto tail_masked = [&](const f32x16& s, int n) __attribute__((always_inline)) {
+    f32x16 r;
+    const int hf = lane_id() >> 5;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = ((j >> 2) * 8 + hf * 4 + (j & 3) >= n) ? -INFINITY : s[j];
+    return r;
+  };
+
   const float scale = p.scale_log2;
   int it = 0;  // tile index within the unit
   bool first_segment = true;
@@ -448,40 +458,48 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         __builtin_amdgcn_sched_barrier(0);
       }
       mfma_v_drain(s_cur);
+      const int n0 = min(kTileTok, cp.t_end - cp.t);
+      if (n0 < kTileTok) s_cur = tail_masked(s_cur, n0);
     }
 
     bool last;
     do {  // tile `it`: its softmax and output product, overlapped with the next tile's scores
-      const int nt = min(kTileTok, cp.t_end - cp.t);
       last = cp.last();
       cp.advance();
-      // The next tile must be in LDS before its scores start; the barrier also frees the stage of
-      // tile it - 1, which is refilled at once.
-      tile_ready(last ? it : it + 1);
       // Copies of tile it + 3 into the stage of tile it - 1.  With four waves, each wave copies one
       // token group (nine 1 KB blocks), one block per four score MFMAs below: 36 copies at once
       // would queue in the address unit and hold every wave for hundreds of cycles.  A ragged tile
       // repeats its last row in place of the missing ones; after the unit's last tile the copies
-      // go to the sink (from the first page, which always exists).
-      const char* sp_base = nullptr;
+      // go to the sink (from the first page, which always exists).  The addresses are worked out
+      // before the wait below, so that the block-table read overlaps it; the copies start after it.
+      const char* sp_base = reinterpret_cast<const char*>(p.cache);
       unsigned sp_lane = 0, sp_lds = 0;
+      int sp_page = 0, sp_tok = 0;
+      bool sp_have = false;
       if constexpr (NW == 4) {
         const int ln = lane_id();
         const int tl = (ln >> 3) ^ (wave & 1);
         const unsigned cl16 = (unsigned)((ln & 7) ^ sigma(tl)) * 16u;
+        sp_have = ld.valid;
         if (ld.valid) {
-          const int page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + ld.t / kPage);
+          sp_page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + ld.t / kPage);
+          sp_tok = ld.t % kPage;
           const int ntl = min(kTileTok, ld.t_end - ld.t);
-          sp_base = reinterpret_cast<const char*>(p.cache) + ((size_t)page * kPage + (ld.t % kPage)) * (kRow * 2);
           sp_lane = (unsigned)min(8 * wave + tl, ntl - 1) * (kRow * 2) + cl16;
           sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it + kStages - 1)] + wave * kPer * 1024;
           ld.advance();
         } else {
-          sp_base = reinterpret_cast<const char*>(p.cache);
           sp_lane = (unsigned)(8 * wave + tl) * (kRow * 2) + cl16;
           sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)sink;
         }
+      }
+      // The next tile must be in LDS before its scores start; the barrier also frees the stage of
+      // tile it - 1.
+      tile_ready(last ? it : it + 1);
+      if constexpr (NW == 4) {
         ++issued;
+        asm volatile("" : "+s"(sp_page));  // the page is first needed here, behind the wait
+        if (sp_have) sp_base += ((size_t)sp_page * kPage + sp_tok) * (kRow * 2);
       } else {
         refill(it);
       }
@@ -502,23 +520,14 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       };
       auto softmax_step = [&](int k) __attribute__((always_inline)) {
         if (k == 0) {
-          if (nt < kTileTok) {  // ragged tile: tokens past the end take no weight
-            const int hf = lane_id() >> 5;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int tok = (j >> 2) * 8 + hf * 4 + (j & 3);
-              if (tok >= nt) s_cur[j] = -INFINITY;
-            }
-          }
-        } else if (k == 1) {
           mt = max3(max3(s_cur[0], s_cur[1], s_cur[2]), max3(s_cur[3], s_cur[4], s_cur[5]),
                     max2(s_cur[6], s_cur[7]));
-        } else if (k == 2) {
+        } else if (k == 1) {
           mt = max3(max3(mt, s_cur[8], s_cur[9]), max3(s_cur[10], s_cur[11], s_cur[12]),
                     max3(s_cur[13], s_cur[14], s_cur[15]));
-        } else if (k == 3) {
+        } else if (k == 2) {
           mt = max_halves(mt) * scale;
-        } else if (k == 4) {
+        } else if (k == 3) {
           if (fresh) {
             m_ref = mt;
             fresh = false;
@@ -531,8 +540,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
             l_sum *= alpha;
             rescale = true;
           }
-        } else if (k < 5 + 8) {
-          softmax_exp(k - 5);
+        } else if (k >= 4 && k < 4 + 8) {
+          softmax_exp(k - 4);
         }
       };
 
@@ -554,7 +563,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         mfma_v_drain(s_nxt);
       } else {
 #pragma unroll
-        for (int k = 0; k < 13; ++k) softmax_step(k);
+        for (int k = 0; k < 12; ++k) softmax_step(k);
 #pragma unroll
         for (int j = 0; j < kCG; ++j) spread_copy(j);
       }
@@ -616,7 +625,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (!last) s_cur = s_nxt;  // the second half of tile it's scores was needed until here
+      if (!last) {  // the second half of tile it's scores was needed until here
+        const int nn = min(kTileTok, cp.t_end - cp.t);  // cp holds tile it + 1 now
+        s_cur = nn < kTileTok ? tail_masked(s_nxt, nn) : s_nxt;
+      }
       ++it;
     } while (!last);
 
