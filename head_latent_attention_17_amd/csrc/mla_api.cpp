@@ -3,6 +3,8 @@
 #include "../../include/mla.h"
 
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "mla_internal.h"
 
@@ -23,6 +25,11 @@ int auto_units(int batch, int heads, int max_blocks) {
 size_t workspace_bytes(int batch, int heads, int units) {
   const size_t parts = ((size_t)units + (size_t)batch) * (size_t)heads;
   return parts * (size_t)kDc * sizeof(float) + parts * 2 * sizeof(float) + (size_t)batch * 4 * sizeof(int);
+}
+
+bool debug_checks_enabled() {
+  const char* v = getenv("MLA_DEBUG_CHECKS");
+  return v && strcmp(v, "1") == 0;
 }
 
 }  // namespace mla
@@ -68,6 +75,12 @@ mla_status mla_cache_append(void* kv_cache, int num_pages, int page_size, const 
   if (batch == 0) return MLA_OK;
   if (num_pages < 1) return MLA_ERR_SHAPE;
   if (!kv_cache || !block_table || !positions || !c_new || !kpe_new) return MLA_ERR_NULL;
+  if (debug_checks_enabled()) {
+    bool bad = false;
+    if (check_tables(block_table, max_blocks_per_seq, positions, batch, num_pages, true, stream, &bad) != hipSuccess)
+      return MLA_ERR_HIP;
+    if (bad) return MLA_ERR_BLOCK_TABLE;
+  }
   hipError_t e = launch_append(kv_cache, block_table, max_blocks_per_seq, positions, c_new, kpe_new,
                                batch, dtype == MLA_F32, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -110,6 +123,12 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
   const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq);
   const size_t need = workspace_bytes(batch, num_heads, units);
   if (!workspace || workspace_bytes_given < need) return MLA_ERR_WORKSPACE;
+  if (debug_checks_enabled()) {
+    bool bad = false;
+    if (check_tables(block_table, max_blocks_per_seq, seq_lens, batch, num_pages, false, stream, &bad) != hipSuccess)
+      return MLA_ERR_HIP;
+    if (bad) return MLA_ERR_BLOCK_TABLE;
+  }
 
   DecodeParams p;
   p.q_abs = q_abs;

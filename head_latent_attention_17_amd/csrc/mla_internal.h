@@ -52,4 +52,11 @@ hipError_t launch_out_proj(const void* o_lat, const void* w_uv, void* out, int b
                            bool f32, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, bool f32, hipStream_t s);
 
+// Device-side check of block-table entries and lengths (append = false) or append positions
+// (append = true); synchronises s.  *bad is set when an entry is out of range.
+hipError_t check_tables(const int32_t* block_table, int max_blocks, const int32_t* lens, int batch,
+                        int num_pages, bool append, hipStream_t s, bool* bad);
+// MLA_DEBUG_CHECKS=1 in the environment, read at every call.
+bool debug_checks_enabled();
+
 }  // namespace mla

@@ -38,7 +38,10 @@
  *     negative mla_status on error, without touching any buffer.  Launch failures are reported as
  *     MLA_ERR_HIP.  Nothing is thrown across the ABI.
  *   - Device-side contents (block-table entries, lengths) are trusted: an entry outside
- *     [0, num_pages) or a length above max_blocks_per_seq * 64 is undefined behaviour.
+ *     [0, num_pages) or a length above max_blocks_per_seq * 64 is undefined behaviour.  With the
+ *     environment variable MLA_DEBUG_CHECKS=1 (read at every call), mla_cache_append and mla_decode
+ *     first check on the device every entry they would use, synchronise the stream to read the
+ *     verdict, and return MLA_ERR_BLOCK_TABLE, launching nothing else, if one is out of range.
  *   - Calls that share a workspace must be ordered on one stream.
  */
 #ifndef MLA_H
@@ -60,7 +63,7 @@ typedef enum {
   MLA_ERR_DTYPE = -3,        /* unknown mla_dtype */
   MLA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than mla_decode_workspace_size() */
   MLA_ERR_UNSUPPORTED = -5,  /* page_size != 64, or heads not in {16, 32, 64, 128} */
-  MLA_ERR_BLOCK_TABLE = -6,  /* reserved for a device-side block-table check */
+  MLA_ERR_BLOCK_TABLE = -6,  /* device-side check (MLA_DEBUG_CHECKS=1): bad table entry or length */
   MLA_ERR_HIP = -7           /* a HIP launch failed */
 } mla_status;
 

@@ -182,3 +182,47 @@ def test_page_permutation_invariance_and_determinism(lib):
         outs.append((g.o_lat.view(torch.int16).clone(), g.lse.clone()))
     for o, l in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(l.view(torch.int32), outs[0][1].view(torch.int32))
+
+
+def test_debug_checks_reject_bad_tables(lib, monkeypatch):
+    """MLA_DEBUG_CHECKS=1: valid tables give the unchecked result bit for bit; a used block-table
+    entry outside [0, num_pages), a length past the table row or an append position past it is
+    reported as MLA_ERR_BLOCK_TABLE before anything else is launched (the cache is left as it was).
+    Bad tables are only ever passed with the check on."""
+    wl = synth.make_custom([70, 5, 130], heads=128, seed=81, append=True)
+    say("debug checks")
+    g = Gpu(wl)
+    g.step(lib, q_abs_from_absorb=False)
+    torch.cuda.synchronize()
+    o_plain = g.o_lat.clone()
+    monkeypatch.setenv("MLA_DEBUG_CHECKS", "1")
+    g.o_lat.zero_()
+    lib.mla_decode(g.q_lat_in, g.cache, g.bt, g.attended, wl.scale, g.o_lat, g.lse, g.workspace(lib), 0)
+    torch.cuda.synchronize()
+    assert torch.equal(g.o_lat.view(torch.int16), o_plain.view(torch.int16))
+
+    def decode_with(bt, lens):
+        lib.mla_decode(g.q_lat_in, g.cache, bt, lens, wl.scale, g.o_lat, g.lse, g.workspace(lib), 0)
+
+    bad = g.bt.clone()
+    bad[1, 0] = wl.num_pages + 5          # the only page of sequence 1
+    neg = g.bt.clone()
+    neg[0, 1] = -1                         # second page of sequence 0 (71 attended tokens)
+    long_lens = g.attended.clone()
+    long_lens[2] = wl.max_blocks * 64 + 1
+    for bt, lens in ((bad, g.attended), (neg, g.attended), (g.bt, long_lens)):
+        with pytest.raises(lib.MLAError) as err:
+            decode_with(bt, lens)
+        assert err.value.status == -6
+
+    before = g.cache.view(torch.int16).clone()
+    far = g.lens.clone()
+    far[0] = wl.max_blocks * 64            # one past the last slot of the row
+    bad_page = g.bt.clone()
+    bad_page[2, int(wl.lens[2]) // 64] = -1
+    for bt, pos in ((g.bt, far), (bad_page, g.lens)):
+        with pytest.raises(lib.MLAError) as err:
+            lib.mla_cache_append(g.cache, bt, pos, g.c_new, g.kpe_new)
+        assert err.value.status == -6
+    torch.cuda.synchronize()
+    assert torch.equal(g.cache.view(torch.int16), before)
