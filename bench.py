@@ -54,10 +54,15 @@ def parse():
     return ap.parse_args()
 
 
+# Sources of the decode call's kernels and of its work split; the traffic record is valid only for
+# the sources it was taken on.
+DECODE_SOURCES = ("decode.hip", "decode_mfma.hip", "mla_api.cpp", "mla_device.h", "mla_internal.h")
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "head_latent_attention_17_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in DECODE_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

@@ -7,8 +7,8 @@
 // slice of W to LDS once and applies it to the whole batch.
 //
 // Work split: one workgroup per (head, 32 NB output columns), so every weight byte is fetched by
-// exactly one workgroup (with NB = 1: 2,048 workgroups for the absorption, 512 for the
-// out-projection).  The workgroup's weight slab (K rows x 64 NB bytes) is copied HBM -> LDS in one
+// exactly one workgroup (1,024 workgroups for the absorption with NB = 2, 512 for the
+// out-projection with NB = 1).  The workgroup's weight slab (K rows x 64 NB bytes) is copied HBM -> LDS in one
 // go with global_load_lds_dwordx4 (1 KB per copy, no registers held), while the batch rows of A are
 // fetched straight into registers.  The four waves split the column blocks and K; partial tiles of
 // one column block are summed through LDS.
@@ -176,10 +176,12 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
   }
 }
 
-// Column blocks per workgroup.  Measured on the MI355X at batch 32 to 128: one block (2,048 and 512
-// workgroups, four K slices) is as fast as or faster than two or four (fewer workgroups, larger slabs).
+// Column blocks per workgroup, measured on the MI355X at batch 4 to 128 with weights that do not
+// stay in the Infinity Cache between calls: two for the absorption (1,024 workgroups, two K slices;
+// 1 us faster than one block at batch 4 and 32, even at 128) and one for the out-projection (512
+// workgroups, four K slices), against one to sixteen blocks.
 #ifndef MLA_NB_ABSORB
-#define MLA_NB_ABSORB 1
+#define MLA_NB_ABSORB 2
 #endif
 #ifndef MLA_NB_OUT
 #define MLA_NB_OUT 1
