@@ -16,12 +16,14 @@
 // ds_read_b64_tr_b16, a 16-lane transposing read.
 //
 // Pipelining.  Tiles stream HBM -> LDS with global_load_lds_dwordx4 through a 4-stage ring, three
-// tiles ahead of the one being processed.  With one wave per SIMD, LDS latency (well over 100
-// cycles under load) is the main stall, so both products prefetch their LDS operands: the score
-// product 4 k-steps ahead (4 x 32 MFMA cycles of cover), the output product two d-blocks ahead,
-// and the first output operands are requested before the softmax so its vector ALU work covers
-// their latency.  The softmax rescale of O is lazy: the reference maximum only moves when a tile's
-// maximum exceeds it by more than 2^8.
+// tiles ahead of the one being processed.  The prologue puts three tiles in flight; after that each
+// wave issues its nine copies of tile it + 3 one per four score MFMAs of tile it + 1.  With one wave
+// per SIMD nothing hides a stall, so one iteration overlaps two tiles: after the wait for tile it + 1
+// (counted vmcnt, then a barrier), the score MFMAs of tile it + 1 carry the softmax of tile it (its
+// maximum, the rescale decision and the first eight exponentials), then the output product of tile
+// it carries the last eight.  LDS operands are prefetched: the score operand 3 k-steps ahead, the
+// output operand 4 d-blocks ahead.  The softmax rescale of O is lazy: the reference maximum only
+// moves when a tile's maximum exceeds it by more than 2^8.
 //
 // Tile layout in LDS.  A tile is 32 tokens x 72 chunks of 16 bytes, stored as 36 blocks of
 // 8 tokens x 8 chunks, 1 KB each (block = 9 (t / 8) + c / 8), so one global_load_lds_dwordx4 fills
@@ -77,7 +79,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Score MFMAs with their accumulator pinned to VGPRs: the 32 x 512 output accumulator of each wave
 // takes all 256 AGPRs.  Hazards the compiler cannot see through asm are padded explicitly: two
@@ -341,7 +342,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;       // which K half of the MFMA operands this lane holds
   const int l32 = lane & 31;
-  const int head = wave * 32 + l32; // head of this lane's score / output column
   const int w = uni(xcd_unit(blockIdx.x, gridDim.x));
 
   TileCursor ld, cp;
