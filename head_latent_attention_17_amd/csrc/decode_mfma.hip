@@ -193,17 +193,39 @@ struct TileCursor {
   }
   __device__ __forceinline__ void init(const DecodeParams& p, int w) {
     lens = p.seq_lens;
-    const int P = uni((int)total_pages(p.seq_lens, p.batch));
-    pg0 = uni((int)((long long)w * P / p.num_units));
-    pg1 = uni((int)((long long)(w + 1) * P / p.num_units));
-    all_live = P >= p.num_units;
-    valid = pg0 < pg1;
-    if (!valid) return;
-    int bb;
-    long long bf;
-    locate_page(p.seq_lens, p.batch, pg0, bb, bf);
-    b = uni(bb);
-    before = uni((int)bf);
+    if (p.batch <= 64) {
+      // One pass: lane i holds sequence i's page count, an inclusive scan gives both the total and
+      // the sequence holding the unit's first page.
+      const int ln = threadIdx.x & 63;
+      const int np_l = ln < p.batch ? (p.seq_lens[ln] + kPage - 1) / kPage : 0;
+      int incl = np_l;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int n = __shfl_up(incl, o, 64);
+        if (ln >= o) incl += n;
+      }
+      const int P = __builtin_amdgcn_readlane(incl, 63);
+      pg0 = uni((int)((long long)w * P / p.num_units));
+      pg1 = uni((int)((long long)(w + 1) * P / p.num_units));
+      all_live = P >= p.num_units;
+      valid = pg0 < pg1;
+      if (!valid) return;
+      const unsigned long long hit = __ballot(ln < p.batch && incl > pg0);
+      b = uni(__ffsll((long long)hit) - 1);
+      before = __builtin_amdgcn_readlane(incl - np_l, b);
+    } else {
+      const int P = uni((int)total_pages(p.seq_lens, p.batch));
+      pg0 = uni((int)((long long)w * P / p.num_units));
+      pg1 = uni((int)((long long)(w + 1) * P / p.num_units));
+      all_live = P >= p.num_units;
+      valid = pg0 < pg1;
+      if (!valid) return;
+      int bb;
+      long long bf;
+      locate_page(p.seq_lens, p.batch, pg0, bb, bf);
+      b = uni(bb);
+      before = uni((int)bf);
+    }
     load_seq();
     enter();
   }
