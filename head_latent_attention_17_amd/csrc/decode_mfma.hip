@@ -178,7 +178,7 @@ struct TileCursor {
 
   __device__ __forceinline__ void load_seq() {
     len = ld_const(lens, b);
-    np = (len + kPage - 1) / kPage;
+    np = (int)(((unsigned)max(len, 0) + kPage - 1) / kPage);
   }
   // Sets t / t_end for sequence b, skipping sequences with no tokens.
   __device__ __forceinline__ void enter() {
@@ -197,7 +197,7 @@ struct TileCursor {
       // One pass: lane i holds sequence i's page count, an inclusive scan gives both the total and
       // the sequence holding the unit's first page.
       const int ln = threadIdx.x & 63;
-      const int np_l = ln < p.batch ? (p.seq_lens[ln] + kPage - 1) / kPage : 0;
+      const int np_l = ln < p.batch ? (int)(((unsigned)max(p.seq_lens[ln], 0) + kPage - 1) / kPage) : 0;
       int incl = np_l;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -280,10 +280,10 @@ template <int NW>
 __device__ __forceinline__ void issue_tile(const DecodeParams& p, const TileCursor& c,
                                            LDS_AS char* stage, int wave) {
   constexpr int kPer = kBlocks / NW;
-  const int page = ld_const(p.block_table, (size_t)c.b * p.max_blocks + c.t / kPage);
+  const int page = ld_const(p.block_table, (size_t)c.b * p.max_blocks + (unsigned)c.t / kPage);
   const int nt = min(kTileTok, c.t_end - c.t);
   const char* base = reinterpret_cast<const char*>(p.cache) +
-                     ((size_t)page * kPage + (c.t % kPage)) * (kRow * 2);
+                     ((size_t)page * kPage + ((unsigned)c.t % kPage)) * (kRow * 2);
   const unsigned lds = (unsigned)(uintptr_t)stage;
   int ln;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
@@ -504,8 +504,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         const unsigned cl16 = (unsigned)((ln & 7) ^ sigma(tl)) * 16u;
         sp_have = ld.valid;
         if (ld.valid) {
-          sp_page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + ld.t / kPage);
-          sp_tok = ld.t % kPage;
+          sp_page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage);
+          sp_tok = (int)((unsigned)ld.t % kPage);
           const int ntl = min(kTileTok, ld.t_end - ld.t);
           sp_lane = (unsigned)min(8 * wave + tl, ntl - 1) * (kRow * 2) + cl16;
           sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it + kStages - 1)] + wave * kPer * 1024;

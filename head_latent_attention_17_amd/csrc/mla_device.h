@@ -60,7 +60,7 @@ __device__ __forceinline__ long long wave_incl_scan_i64(long long v) {
 // planning launch are needed.
 // ---------------------------------------------------------------------------------------------
 
-__device__ __forceinline__ int pages_of(int len) { return (len + kPage - 1) / kPage; }
+__device__ __forceinline__ int pages_of(int len) { return (int)(((unsigned)max(len, 0) + kPage - 1) / kPage); }
 
 __device__ __forceinline__ long long unit_start(long long total_pages, int num_units, int w) {
   return (long long)w * total_pages / num_units;
