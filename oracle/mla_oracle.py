@@ -234,6 +234,44 @@ def _f64(x) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------------------
+# The producer side of the cache (explainer Step 5, eq. 9; Step 7)
+# --------------------------------------------------------------------------------------------------
+
+
+def rope_rotate(x, position, base: float) -> np.ndarray:
+    """Rotary position embedding of one vector (explainer Step 7: each query and key is rotated by an
+    angle proportional to its position, so that a score depends only on how far apart the two tokens
+    are).  Reading -- the pages give neither the frequencies nor the pairing: consecutive pairs
+    (x[2i], x[2i+1]) turn by position * base^(-2i/d) radians, the plain rotary form with no
+    context-extension rescaling."""
+    x = _f64(x)
+    d = x.shape[-1]
+    out = np.empty_like(x)
+    for i in range(d // 2):
+        angle = float(position) * base ** (-2.0 * i / d)
+        c, s = math.cos(angle), math.sin(angle)
+        out[..., 2 * i] = x[..., 2 * i] * c - x[..., 2 * i + 1] * s
+        out[..., 2 * i + 1] = x[..., 2 * i] * s + x[..., 2 * i + 1] * c
+    return out
+
+
+def latent_row(h, w_dkv, w_kr, position, base: float) -> np.ndarray:
+    """The cache row one token contributes, [c | k^R] (explainer Step 5, eq. 9: the hidden vector is
+    squeezed to the latent note c = W^DKV h, 5,120 -> 512; Step 7: plus one 64-dim rotated key k^R
+    shared by all heads).  Reading: k^R = RoPE(W^KR h) with W^KR a 5,120 -> 64 projection; the
+    weights are stored [5120][512] and [5120][64], so both products are h @ W."""
+    h = _f64(h)
+    c = h @ _f64(w_dkv)
+    k = rope_rotate(h @ _f64(w_kr), position, base)
+    return np.concatenate([c, k])
+
+
+def latent_rows_batch(h, w_dkv, w_kr, positions, base: float) -> np.ndarray:
+    """latent_row for every sequence b: token positions[b] with hidden vector h[b]; [B][576]."""
+    return np.stack([latent_row(h[b], w_dkv, w_kr, int(positions[b]), base) for b in range(len(positions))])
+
+
+# --------------------------------------------------------------------------------------------------
 # Cache arithmetic (explainer Steps 2 and 8; wiki "KV cache compression")
 # --------------------------------------------------------------------------------------------------
 

@@ -337,3 +337,60 @@ def test_bf16_widening_is_exact():
     assert vals[2] == 3.140625
     assert vals[5] == float(np.float32(3.3895313892515355e38))
     assert vals[6] == 2.0 ** -133
+
+
+# --------------------------------------------------------------------------------------------------
+# The producer side of the cache: eq. 9 (explainer Step 5) and the rotated key (Step 7)
+# --------------------------------------------------------------------------------------------------
+
+def test_rope_closed_forms():
+    """Hand-computable rotations (d = 4, base 100, so the two pairs turn at 1 and 0.1 rad per
+    position): a wrong sign, pairing or frequency exponent fails one of these."""
+    c1, s1 = math.cos(1.0), math.sin(1.0)
+    # pair 0 of e_0 at position 1 turns by 1 rad
+    assert np.allclose(O.rope_rotate([1.0, 0.0, 0.0, 0.0], 1, 100.0), [c1, s1, 0, 0], atol=1e-15)
+    # pair 0 of e_1: (0, 1) -> (-sin, cos)
+    assert np.allclose(O.rope_rotate([0.0, 1.0, 0.0, 0.0], 1, 100.0), [-s1, c1, 0, 0], atol=1e-15)
+    # pair 1 (dims 2, 3) turns at 100^(-2/4) = 0.1 rad per position: 1 rad at position 10
+    assert np.allclose(O.rope_rotate([0.0, 0.0, 1.0, 0.0], 10, 100.0), [0, 0, c1, s1], atol=1e-15)
+    assert np.allclose(O.rope_rotate([0.0, 0.0, 0.0, 1.0], 10, 100.0), [0, 0, -s1, c1], atol=1e-15)
+    # position 0 is the identity, exactly
+    x = np.random.default_rng(3).normal(size=64)
+    assert np.array_equal(O.rope_rotate(x, 0, 10000.0), x)
+
+
+def test_rope_scores_depend_only_on_distance():
+    """The property the explainer states for RoPE (Step 7): a rotated query-key score depends on the
+    positions only through their difference; rotations also keep lengths and compose."""
+    rng = np.random.default_rng(5)
+    q, k = rng.normal(size=64), rng.normal(size=64)
+    base = 10000.0
+    for m, n, shift in ((3, 17, 1000), (0, 131072, 7), (91204, 5, 40000)):
+        a = O.rope_rotate(q, m, base) @ O.rope_rotate(k, n, base)
+        b = O.rope_rotate(q, m + shift, base) @ O.rope_rotate(k, n + shift, base)
+        c = q @ O.rope_rotate(k, n - m, base)
+        assert abs(a - b) <= 1e-9 * (abs(a) + 1) and abs(a - c) <= 1e-9 * (abs(a) + 1)
+    for pos in (1, 77, 131071):
+        r = O.rope_rotate(q, pos, base)
+        assert np.allclose(np.hypot(r[0::2], r[1::2]), np.hypot(q[0::2], q[1::2]), rtol=1e-12)
+    assert np.allclose(O.rope_rotate(O.rope_rotate(q, 1234, base), 4321, base),
+                       O.rope_rotate(q, 5555, base), atol=1e-9)
+
+
+def test_latent_row_vs_brute_force():
+    """eq. 9 and the rotated key with explicit loops on a tiny non-square shape (a transposed weight
+    fails): d_model 6, d_c 4, d_R 2."""
+    rng = np.random.default_rng(9)
+    h = rng.normal(size=6)
+    w_dkv = rng.normal(size=(6, 4))
+    w_kr = rng.normal(size=(6, 2))
+    pos, base = 3, 10000.0
+    row = O.latent_row(h, w_dkv, w_kr, pos, base)
+    c = [sum(h[i] * w_dkv[i, j] for i in range(6)) for j in range(4)]
+    k = [sum(h[i] * w_kr[i, j] for i in range(6)) for j in range(2)]
+    ang = pos * base ** 0.0                      # one pair: frequency base^0 = 1
+    kr = [k[0] * math.cos(ang) - k[1] * math.sin(ang), k[0] * math.sin(ang) + k[1] * math.cos(ang)]
+    assert np.allclose(row, c + kr, rtol=1e-13, atol=1e-13)
+    rows = O.latent_rows_batch(np.stack([h, -h]), w_dkv, w_kr, [pos, 0], base)
+    assert np.allclose(rows[0], row) and np.allclose(rows[1, :4], -np.array(c))
+    assert np.allclose(rows[1, 4:], -np.array(k))      # position 0: no rotation
