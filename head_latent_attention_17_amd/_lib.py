@@ -19,7 +19,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTY
           -4: "MLA_ERR_WORKSPACE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_BLOCK_TABLE",
           -7: "MLA_ERR_HIP"}
 EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", "mla_cache_append",
-           "mla_absorb_q", "mla_decode", "mla_out_proj")
+           "mla_absorb_q", "mla_decode", "mla_out_proj", "mla_cache_append_hidden_workspace_size",
+           "mla_cache_append_hidden")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run head_latent_attention_17_amd.build.build()")
@@ -41,6 +42,10 @@ lib.mla_decode.restype = _i
 lib.mla_decode.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _p, _sz, _i, _i, _p]
 lib.mla_out_proj.restype = _i
 lib.mla_out_proj.argtypes = [_p, _p, _p, _i, _i, _i, _p]
+lib.mla_cache_append_hidden_workspace_size.restype = _sz
+lib.mla_cache_append_hidden_workspace_size.argtypes = [_i, _i]
+lib.mla_cache_append_hidden.restype = _i
+lib.mla_cache_append_hidden.argtypes = [_p, _i, _i, _p, _i, _p, _p, _p, _p, _f, _i, _p, _sz, _i, _p]
 
 
 class MLAError(RuntimeError):
@@ -99,6 +104,24 @@ def mla_cache_append(kv_cache, block_table, positions, c_new, kpe_new, stream=No
                                 _ptr(block_table), block_table.shape[1], _ptr(positions),
                                 _ptr(c_new), _ptr(kpe_new), positions.shape[0], _dtype_of(c_new),
                                 _stream(stream)), "mla_cache_append")
+
+
+def mla_cache_append_hidden_workspace_size(batch: int, dtype: int = MLA_BF16) -> int:
+    return int(lib.mla_cache_append_hidden_workspace_size(batch, dtype))
+
+
+def mla_cache_append_hidden(kv_cache, block_table, positions, hidden, w_dkv, w_kr, rope_base=10000.0,
+                            workspace=None, stream=None):
+    """Rows [hidden @ w_dkv | RoPE(hidden @ w_kr)] written at positions (the lengths before the
+    append).  hidden [B][5120], w_dkv [5120][512], w_kr [5120][64] (bf16, or fp32 for the debug
+    mode); workspace: a byte tensor of at least mla_cache_append_hidden_workspace_size(B) bytes."""
+    _dev(kv_cache, block_table, positions, hidden, w_dkv, w_kr, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.mla_cache_append_hidden(_ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1],
+                                       _ptr(block_table), block_table.shape[1], _ptr(positions),
+                                       _ptr(hidden), _ptr(w_dkv), _ptr(w_kr), float(rope_base),
+                                       positions.shape[0], _ptr(workspace), ws_bytes, _dtype_of(hidden),
+                                       _stream(stream)), "mla_cache_append_hidden")
 
 
 def mla_absorb_q(q, w_uk, q_abs, stream=None):

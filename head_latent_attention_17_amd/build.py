@@ -12,7 +12,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libmla.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["mla_api.cpp", "proj.hip", "proj_mfma.hip", "decode.hip", "decode_mfma.hip", "checks.hip"]
+SOURCES = ["mla_api.cpp", "proj.hip", "proj_mfma.hip", "decode.hip", "decode_mfma.hip", "checks.hip",
+           "producer.hip"]
 ARCH = "gfx950"
 
 

@@ -27,6 +27,9 @@ size_t workspace_bytes(int batch, int heads, int units) {
   return parts * (size_t)kDc * sizeof(float) + parts * 2 * sizeof(float) + (size_t)batch * 4 * sizeof(int);
 }
 
+// Ten fp32 partial rows of 576 per sequence (the split of the 5,120-long products).
+size_t append_hidden_workspace_bytes(int batch) { return (size_t)batch * 10 * kRow * sizeof(float); }
+
 bool debug_checks_enabled() {
   const char* v = getenv("MLA_DEBUG_CHECKS");
   return v && strcmp(v, "1") == 0;
@@ -55,7 +58,7 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_abi_version(void) { return 100; }
+int mla_abi_version(void) { return 101; }
 
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype) {
@@ -83,6 +86,36 @@ mla_status mla_cache_append(void* kv_cache, int num_pages, int page_size, const 
   }
   hipError_t e = launch_append(kv_cache, block_table, max_blocks_per_seq, positions, c_new, kpe_new,
                                batch, dtype == MLA_F32, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_cache_append_hidden_workspace_size(int batch, mla_dtype dtype) {
+  if (batch < 0 || !valid_dtype(dtype)) return 0;
+  return append_hidden_workspace_bytes(batch);
+}
+
+mla_status mla_cache_append_hidden(void* kv_cache, int num_pages, int page_size, const int32_t* block_table,
+                                   int max_blocks_per_seq, const int32_t* positions, const void* hidden,
+                                   const void* w_dkv, const void* w_kr, float rope_base, int batch,
+                                   void* workspace, size_t workspace_bytes_given, mla_dtype dtype,
+                                   hipStream_t stream) {
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
+  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (num_pages < 1) return MLA_ERR_SHAPE;
+  if (!kv_cache || !block_table || !positions || !hidden || !w_dkv || !w_kr) return MLA_ERR_NULL;
+  if (!workspace || workspace_bytes_given < append_hidden_workspace_bytes(batch)) return MLA_ERR_WORKSPACE;
+  if (debug_checks_enabled()) {
+    bool bad = false;
+    if (check_tables(block_table, max_blocks_per_seq, positions, batch, num_pages, true, stream, &bad) != hipSuccess)
+      return MLA_ERR_HIP;
+    if (bad) return MLA_ERR_BLOCK_TABLE;
+  }
+  hipError_t e = launch_append_hidden(kv_cache, block_table, max_blocks_per_seq, positions, hidden, w_dkv,
+                                      w_kr, (double)rope_base, batch, static_cast<float*>(workspace),
+                                      dtype == MLA_F32, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

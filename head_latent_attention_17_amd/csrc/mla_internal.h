@@ -51,6 +51,13 @@ hipError_t launch_absorb(const void* q, const void* w_uk, void* q_abs, int batch
 hipError_t launch_out_proj(const void* o_lat, const void* w_uv, void* out, int batch, int heads,
                            bool f32, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, bool f32, hipStream_t s);
+// Producer side: rows [h W_DKV | RoPE(h W_KR)] written at positions[b]; part is the fp32 workspace
+// of append_hidden_workspace_bytes(batch).
+hipError_t launch_append_hidden(void* cache, const int32_t* block_table, int max_blocks,
+                                const int32_t* positions, const void* hidden, const void* w_dkv,
+                                const void* w_kr, double rope_base, int batch, float* part, bool f32,
+                                hipStream_t s);
+size_t append_hidden_workspace_bytes(int batch);
 
 // Device-side check of block-table entries and lengths (append = false) or append positions
 // (append = true); synchronises s.  *bad is set when an entry is out of range.

@@ -104,6 +104,29 @@ mla_status mla_cache_append(void* kv_cache, int num_pages, int page_size, const 
                             const void* kpe_new, int batch, mla_dtype dtype, hipStream_t stream);
 
 /*
+ * The producer side of the cache (explainer Step 5, eq. 9: the hidden vector is squeezed to the
+ * latent note c = W^DKV h, 5,120 -> 512; Step 7: the token also contributes one 64-dim key k^R,
+ * rotated by its position and shared by all heads).  For each b, with p = positions[b] (the length
+ * before the append), the row [hidden[b] @ w_dkv (512) | RoPE_p(hidden[b] @ w_kr) (64)] is rounded
+ * to bf16 (nearest even) and written to page block_table[b][p / 64], slot p % 64.
+ *   hidden  [batch][5120], w_dkv [5120][512], w_kr [5120][64]: bf16 for MLA_BF16 (fp32 accumulation),
+ *           fp32 arrays holding bf16-representable values for MLA_F32 (fp32 arithmetic throughout).
+ *   RoPE_p  (a reading: the pages give neither frequencies nor pairing) turns pair (2i, 2i + 1) by
+ *           p * rope_base^(-2i / 64) radians, computed in double precision; rope_base > 1 (10000 is
+ *           the plain rotary choice), no context-extension rescaling.
+ *   workspace: at least mla_cache_append_hidden_workspace_size(batch, dtype) bytes of device
+ *           memory, contents irrelevant, used only during the call (stream-ordered).
+ * Errors as mla_cache_append, plus MLA_ERR_SHAPE for a bad rope_base and MLA_ERR_WORKSPACE.  With
+ * MLA_DEBUG_CHECKS=1 the positions and table entries are checked as for mla_cache_append.
+ */
+size_t mla_cache_append_hidden_workspace_size(int batch, mla_dtype dtype);
+mla_status mla_cache_append_hidden(void* kv_cache, int num_pages, int page_size, const int32_t* block_table,
+                                   int max_blocks_per_seq, const int32_t* positions, const void* hidden,
+                                   const void* w_dkv, const void* w_kr, float rope_base, int batch,
+                                   void* workspace, size_t workspace_bytes, mla_dtype dtype,
+                                   hipStream_t stream);
+
+/*
  * Absorb the content query into latent space (explainer Step 6):
  *   q_abs[b][h][0:512]   = q[b][h][0:128] @ W_UK[h]     (fp32 accumulation)
  *   q_abs[b][h][512:576] = q[b][h][128:192]             (q^R passes through, explainer Step 7)

@@ -34,10 +34,12 @@ D_NOPE = 128     # per-head content query/key width (explainer Step 2: 128-dim h
 D_V = 128        # per-head value width (explainer Step 2)
 ROW = D_C + D_R  # numbers per cached token per layer (explainer Step 8)
 PAGE = 64        # tokens per cache page (the library's fixed page size)
+D_MODEL = 5120   # hidden width a token's cache row is projected from
 Q_DIM = D_NOPE + D_R
 
 # stream ids (one independent counter stream per kind of input)
 S_CACHE, S_Q, S_QABS, S_WUK, S_WUV, S_NEWROW, S_GARBAGE = 1, 2, 3, 4, 5, 6, 7
+S_HIDDEN, S_WDKV, S_WKR = 8, 9, 10
 
 _U64 = (1 << 64) - 1
 _GAMMA = 0x9E3779B97F4A7C15
@@ -280,6 +282,21 @@ def new_rows(wl: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
     n = wl.batch * ROW
     return normal_bf16(stream_key(wl.seed, S_NEWROW, layer), _idx(n, device), 1.0).view(
         wl.batch, ROW)
+
+
+def hidden_states(wl: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
+    """Hidden vectors of the tokens being appended, N(0,1), int16 [B][5120]."""
+    n = wl.batch * D_MODEL
+    return normal_bf16(stream_key(wl.seed, S_HIDDEN, layer), _idx(n, device), 1.0).view(wl.batch, D_MODEL)
+
+
+def producer_weights(wl: Workload, layer: int = 0, device="cpu"):
+    """W_DKV int16 [5120][512] and W_KR int16 [5120][64], std 1/sqrt(5120) (both read the 5,120-wide
+    hidden vector, so the latent and the key come out near unit variance)."""
+    std = 1.0 / math.sqrt(D_MODEL)
+    w_dkv = normal_bf16(stream_key(wl.seed, S_WDKV, layer), _idx(D_MODEL * D_C, device), std).view(D_MODEL, D_C)
+    w_kr = normal_bf16(stream_key(wl.seed, S_WKR, layer), _idx(D_MODEL * D_R, device), std).view(D_MODEL, D_R)
+    return w_dkv, w_kr
 
 
 def as_bf16(t: torch.Tensor) -> torch.Tensor:

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.mla_abi_version() == 100
+    assert L.mla_abi_version() == 101
     for code, name in L.STATUS.items():
         assert L.mla_status_string(code).startswith(name)
     assert "unknown" in L.mla_status_string(12345)
@@ -107,6 +107,32 @@ def test_projection_and_append_validation():
     assert L.lib.mla_cache_append(FAKE, 8, 16, FAKE, 1, FAKE, FAKE, FAKE, 2, 0, None) == -5
     assert L.lib.mla_cache_append(FAKE, 8, 64, FAKE, 1, None, FAKE, FAKE, 2, 0, None) == -1
     assert L.lib.mla_cache_append(FAKE, 0, 64, FAKE, 1, FAKE, FAKE, FAKE, 2, 0, None) == -2
+
+
+def test_append_hidden_validation_and_workspace():
+    """The producer-side append: workspace formula (ten fp32 partial rows of 576 per sequence) and
+    host-side validation, each failing before anything is launched."""
+    L = _lib()
+    assert L.mla_cache_append_hidden_workspace_size(32) == 32 * 10 * 576 * 4
+    assert L.mla_cache_append_hidden_workspace_size(-1) == 0
+    assert L.mla_cache_append_hidden_workspace_size(4, 7) == 0
+    f = L.lib.mla_cache_append_hidden
+    ws = 2 * 10 * 576 * 4
+    ok = [FAKE, 8, 64, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 10000.0, 2, FAKE, ws, 0, None]
+    def call(**kw):
+        args = list(ok)
+        names = ["cache", "pages", "page", "bt", "mb", "pos", "h", "wd", "wk", "base", "batch", "ws", "wsb", "dt", "s"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+    assert call(batch=0, cache=None) == 0           # empty batch: nothing to do
+    assert call(dt=9) == -3
+    assert call(page=16) == -5
+    assert call(batch=-1) == -2
+    assert call(base=1.0) == -2 and call(base=float("nan")) == -2 and call(base=float("inf")) == -2
+    assert call(pages=0) == -2
+    assert call(h=None) == -1 and call(wk=None) == -1
+    assert call(ws=None) == -4 and call(wsb=ws - 1) == -4
 
 
 def test_python_binding_rejects_host_tensors():

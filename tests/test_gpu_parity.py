@@ -226,3 +226,41 @@ def test_debug_checks_reject_bad_tables(lib, monkeypatch):
         assert err.value.status == -6
     torch.cuda.synchronize()
     assert torch.equal(g.cache.view(torch.int16), before)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_append_hidden_matches_oracle(lib, f32):
+    """Producer side of the cache (explainer Step 5, eq. 9, and Step 7): the row
+    [h W_DKV | RoPE_p(h W_KR)] written at each sequence's next position, against the float64
+    oracle, within one bf16 rounding of it (plus fp32 accumulation); positions up to 131,071 give
+    large rotation angles.  Every other cache byte is left as it was, and a repeat is bit-identical."""
+    lens = [0, 1, 63, 64, 200, 4095, 131071]
+    wl = synth.make_custom(lens, heads=16, seed=91, append=True)
+    say("append hidden", "f32" if f32 else "bf16")
+    dev = "cuda"
+    cache = synth.cache_pages(wl, 0, device=dev, chunk_pages=2048).view(torch.bfloat16)
+    bt = torch.as_tensor(wl.block_table, device=dev)
+    pos = torch.as_tensor(wl.lens, device=dev)
+    h_bits = synth.hidden_states(wl, 0, device=dev)
+    wd_bits, wk_bits = synth.producer_weights(wl, 0, device=dev)
+    h, wd, wk = act(h_bits, f32), act(wd_bits, f32), act(wk_bits, f32)
+    ws = torch.empty(lib.mla_cache_append_hidden_workspace_size(wl.batch), dtype=torch.uint8, device=dev)
+    before = cache.view(torch.int16).clone()
+    lib.mla_cache_append_hidden(cache, bt, pos, h, wd, wk, 10000.0, ws)
+    torch.cuda.synchronize()
+    after = cache.view(torch.int16).clone()
+    pages = [int(wl.block_table[b][lens[b] // 64]) for b in range(wl.batch)]
+    slots = [lens[b] % 64 for b in range(wl.batch)]
+    keep = torch.ones(cache.shape[:2], dtype=torch.bool, device=dev)
+    keep[pages, slots] = False
+    assert torch.equal(after[keep], before[keep])
+    got = O.bf16_to_f64(after[pages, slots].cpu().numpy())
+    ref = O.latent_rows_batch(synth.to_numpy_u16(h_bits), synth.to_numpy_u16(wd_bits),
+                              synth.to_numpy_u16(wk_bits), wl.lens, 10000.0)
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max(axis=1, keepdims=True)
+    say(f"  max err / bound {float((err / bound).max()):.3f}")
+    assert (err <= bound).all()
+    lib.mla_cache_append_hidden(cache, bt, pos, h, wd, wk, 10000.0, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.view(torch.int16), after)
