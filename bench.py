@@ -34,6 +34,8 @@ METRIC = "MLA decode: latent-cache GB/s, TFLOP/s, tokens/s; % of HBM/MFMA roofli
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TF = 2500.0   # MI355X dense bf16 MFMA
 ROW_BYTES = 1152
+ROW_ELEMS = 576
+D_MODEL = 5120
 D_C, D_R, D_NOPE, D_V = 512, 64, 128, 128
 
 
@@ -81,6 +83,62 @@ def traffic_record(workload: str):
     if rec.get("kernel_source_sha") != kernel_source_sha():
         return None
     return rec
+
+
+def producer_timing(lib, synth, wl, dev, cache, bt, lens, steps: int):
+    """The producer side of the cache on the same batch: mla_cache_append_hidden writing each
+    sequence's next row ([h W_DKV | RoPE(h W_KR)], the slots the step's append fills), with the
+    weights rotated through more copies than the Infinity Cache holds.  One call per weight copy is
+    captured in a HIP graph and the graph is replayed, timed with HIP events around the replays: the
+    Python marshalling of a call (longer than the call's GPU time at this batch) is not what is
+    timed.  The rows the replays leave are checked bit for bit against an eager call with the last
+    weights.  bytes = weights + hidden rows + written rows."""
+    import torch
+    h = synth.hidden_states(wl, 0, device=dev).view(torch.bfloat16)
+    copies = 48                                   # 48 x 5.9 MB > 256 MB
+    wts = [tuple(w.view(torch.bfloat16) for w in synth.producer_weights(wl, 1000 + i, device=dev))
+           for i in range(copies)]
+    ws = torch.empty(lib.mla_cache_append_hidden_workspace_size(wl.batch), dtype=torch.uint8, device=dev)
+    b_idx = torch.arange(wl.batch, device=dev)
+    page_of = bt[b_idx, lens.long() // 64].long()
+    slots = (page_of * 64 + lens.long() % 64)
+
+    def written():
+        return cache.view(-1, ROW_ELEMS)[slots].clone()
+
+    lib.mla_cache_append_hidden(cache, bt, lens, h, *wts[copies - 1], 10000.0, ws)
+    torch.cuda.synchronize()
+    expect = written()
+    for i in range(copies):
+        lib.mla_cache_append_hidden(cache, bt, lens, h, *wts[i], 10000.0, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(copies):
+            lib.mla_cache_append_hidden(cache, bt, lens, h, *wts[i], 10000.0, ws)
+    torch.cuda.synchronize()
+    replays = max(2, -(-steps // copies))
+    for _ in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(written(), expect):
+            raise RuntimeError("graph replay of mla_cache_append_hidden wrote other rows than an eager call")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    if not torch.equal(written(), expect):
+        raise RuntimeError("graph replay of mla_cache_append_hidden wrote other rows than an eager call")
+    ms = a.elapsed_time(b) / (replays * copies)
+    del g
+    nbytes = D_MODEL * ROW_ELEMS * 2 + wl.batch * D_MODEL * 2 + wl.batch * ROW_BYTES
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"call": "mla_cache_append_hidden", "batch": wl.batch, "ms_per_call": round(ms, 5),
+            "bytes": nbytes, "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "weights": "48 rotated copies, cold", "timing": "graph replay"}
 
 
 def cpu_baseline(wl, seconds: float):
@@ -308,6 +366,8 @@ def main():
                      "mfma_tflops": round(dec_tf, 2),
                      "mfma_frac": round(dec_tf / MFMA_BF16_PEAK_TF, 4)},
     }
+    if wl.append:  # the table has a slot at each sequence's next position only when the workload appends
+        line["producer"] = producer_timing(lib, synth, wl, dev, inst[0]["cache"], bt, lens, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -27,8 +27,8 @@ size_t workspace_bytes(int batch, int heads, int units) {
   return parts * (size_t)kDc * sizeof(float) + parts * 2 * sizeof(float) + (size_t)batch * 4 * sizeof(int);
 }
 
-// Ten fp32 partial rows of 576 per sequence (the split of the 5,120-long products).
-size_t append_hidden_workspace_bytes(int batch) { return (size_t)batch * 10 * kRow * sizeof(float); }
+// Twenty fp32 partial rows of 576 per sequence (the split of the 5,120-long products).
+size_t append_hidden_workspace_bytes(int batch) { return (size_t)batch * kAppendChunks * kRow * sizeof(float); }
 
 bool debug_checks_enabled() {
   const char* v = getenv("MLA_DEBUG_CHECKS");

@@ -15,6 +15,7 @@ constexpr int kRow = 576;     // cached numbers per token
 constexpr int kQdim = 192;    // [q_nope | q_pe]
 constexpr int kPage = 64;     // tokens per page
 constexpr int kNumCUs = 256;  // MI355X compute units (used only to pick the automatic split)
+constexpr int kAppendChunks = 20;  // 5,120 / 256: partial sums per output of the producer products
 
 // Everything a decode launch needs.  Pointers are device pointers.
 struct DecodeParams {

@@ -113,11 +113,11 @@ def test_append_hidden_validation_and_workspace():
     """The producer-side append: workspace formula (ten fp32 partial rows of 576 per sequence) and
     host-side validation, each failing before anything is launched."""
     L = _lib()
-    assert L.mla_cache_append_hidden_workspace_size(32) == 32 * 10 * 576 * 4
+    assert L.mla_cache_append_hidden_workspace_size(32) == 32 * 20 * 576 * 4
     assert L.mla_cache_append_hidden_workspace_size(-1) == 0
     assert L.mla_cache_append_hidden_workspace_size(4, 7) == 0
     f = L.lib.mla_cache_append_hidden
-    ws = 2 * 10 * 576 * 4
+    ws = 2 * 20 * 576 * 4
     ok = [FAKE, 8, 64, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 10000.0, 2, FAKE, ws, 0, None]
     def call(**kw):
         args = list(ok)
