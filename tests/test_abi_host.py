@@ -110,7 +110,7 @@ def test_projection_and_append_validation():
 
 
 def test_append_hidden_validation_and_workspace():
-    """The producer-side append: workspace formula (ten fp32 partial rows of 576 per sequence) and
+    """The producer-side append: workspace formula (twenty fp32 partial rows of 576 per sequence) and
     host-side validation, each failing before anything is launched."""
     L = _lib()
     assert L.mla_cache_append_hidden_workspace_size(32) == 32 * 20 * 576 * 4
