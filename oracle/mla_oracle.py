@@ -32,7 +32,9 @@ Readings where the pages are silent (each also listed in the design notes):
   * decode has one query that attends to every cached token of its sequence, position 0 .. len-1,
     including the row appended this step -- no mask inside that range;
   * a sequence of length 0 yields o = 0 and lse = -inf;
-  * lse is the natural log of the softmax denominator of the *scaled* scores.
+  * lse is the natural log of the softmax denominator of the *scaled* scores;
+  * the ~6-bit cache (the explainer's audit after Step 8 gives only "about six bits" per number) is
+    FP6 E2M3 codes with one power-of-two scale per row, rounded to nearest with ties to even.
 
 Every function here is pinned by a test in ``tests/test_oracle_*.py`` against the explainer's worked
 2-D example (Step 6), its cache arithmetic (Steps 2 and 8), brute-force loops on tiny shapes, closed
@@ -269,6 +271,131 @@ def latent_row(h, w_dkv, w_kr, position, base: float) -> np.ndarray:
 def latent_rows_batch(h, w_dkv, w_kr, positions, base: float) -> np.ndarray:
     """latent_row for every sequence b: token positions[b] with hidden vector h[b]; [B][576]."""
     return np.stack([latent_row(h[b], w_dkv, w_kr, int(positions[b]), base) for b in range(len(positions))])
+
+
+# --------------------------------------------------------------------------------------------------
+# A ~6-bit cache (explainer, the audit after Step 8: deployed V2 stores each cached number in about
+# six bits, near 26 KB per token over its 60 layers).  The pages give no format; the reading here:
+# each number is an FP6 E2M3 code (1 sign, 2 exponent, 3 mantissa bits, exponent bias 1, no
+# infinities or NaN: magnitudes 0, 1/8 .. 7/8, then 1 .. 7.5), and each cached row carries one
+# power-of-two scale, so a stored number is code_value * 2^e exactly.
+# --------------------------------------------------------------------------------------------------
+
+FP6_ROW_BYTES = 576 * 6 // 8                   # 432: the row's codes, code i at bits 6i .. 6i+5
+FP6_PAGE_TOKENS = 64
+FP6_PAGE_BYTES = FP6_PAGE_TOKENS * FP6_ROW_BYTES + FP6_PAGE_TOKENS * 4   # rows, then 64 fp32 scales
+FP6_MAX = 7.5
+FP6_MIN_EXP = -126                             # scales stay normal float32 numbers
+
+
+def fp6_e2m3_value(code: int) -> float:
+    """The number a 6-bit E2M3 code stands for, from the format's fields: exponent field 0 is the
+    subnormal range m/8; exponent field e > 0 is (1 + m/8) * 2^(e - 1)."""
+    sign = -1.0 if code & 0b100000 else 1.0
+    e = (code >> 3) & 0b11
+    m = code & 0b111
+    mag = m / 8.0 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 1)
+    return sign * mag
+
+
+FP6_VALUES = np.array([fp6_e2m3_value(c) for c in range(64)])
+
+
+def fp6_e2m3_round(y) -> np.ndarray:
+    """Codes of the E2M3 numbers nearest to y (float64 array): ties go to the code with an even
+    mantissa, magnitudes beyond 7.5 saturate to 7.5, and the sign is kept (also for zero).  Written
+    as a search over the 32 magnitudes, not as bit arithmetic."""
+    y = np.asarray(y, dtype=np.float64)
+    mags = FP6_VALUES[:32]                      # codes 0 .. 31, increasing magnitudes
+    a = np.minimum(np.abs(y), FP6_MAX)
+    dist = np.abs(a[..., None] - mags)
+    best = dist.min(axis=-1, keepdims=True)
+    tied = dist == best                         # one or two neighbouring codes
+    even = tied & (np.arange(32) % 2 == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(tied, axis=-1))
+    return (code | np.where(np.signbit(y), 32, 0)).astype(np.uint8)
+
+
+def fp6_row_exponent(amax: float) -> int:
+    """The smallest e >= -126 with amax <= 7.5 * 2^e: the row's largest magnitude then maps into
+    (3.75, 7.5] and nothing saturates (a row of zeros takes e = -126)."""
+    e = FP6_MIN_EXP
+    while amax > FP6_MAX * 2.0 ** e:
+        e += 1
+    return e
+
+
+def quantize_row_fp6(row) -> tuple[np.ndarray, int]:
+    """(codes [576], e) of one cached row: codes round row / 2^e to the nearest E2M3 numbers.  Dividing
+    by a power of two is exact, so the only rounding is the code choice."""
+    x = _f64(row)
+    e = fp6_row_exponent(float(np.max(np.abs(x))) if x.size else 0.0)
+    return fp6_e2m3_round(x / 2.0 ** e), e
+
+
+def pack_fp6(codes) -> np.ndarray:
+    """Codes [..., n] (n a multiple of 4) -> bytes [..., 3n/4]: code i occupies bits 6i .. 6i+5 of the
+    little-endian bit string (bit k of the string is bit k % 8 of byte k // 8)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    bits = (codes[..., :, None] >> np.arange(6)) & 1          # [..., n, 6], least significant first
+    bits = bits.reshape(*codes.shape[:-1], -1, 8)             # [..., 3n/4, 8]
+    return (bits << np.arange(8)).sum(axis=-1).astype(np.uint8)
+
+
+def unpack_fp6(data) -> np.ndarray:
+    """Inverse of pack_fp6."""
+    data = np.asarray(data, dtype=np.uint8)
+    bits = (data[..., :, None] >> np.arange(8)) & 1
+    bits = bits.reshape(*data.shape[:-1], -1, 6)
+    return (bits << np.arange(6)).sum(axis=-1).astype(np.uint8)
+
+
+def quantize_pages_fp6(pages) -> np.ndarray:
+    """bf16 pages [n][64][576] -> fp6 pages [n][27904] bytes: 64 packed rows of 432 bytes, then the
+    64 row scales 2^e as little-endian float32."""
+    pages = np.asarray(pages)
+    n = pages.shape[0]
+    out = np.zeros((n, FP6_PAGE_BYTES), np.uint8)
+    for i in range(n):
+        scales = np.empty(FP6_PAGE_TOKENS, np.float32)
+        for t in range(FP6_PAGE_TOKENS):
+            codes, e = quantize_row_fp6(pages[i, t])
+            out[i, t * FP6_ROW_BYTES:(t + 1) * FP6_ROW_BYTES] = pack_fp6(codes)
+            scales[t] = 2.0 ** e
+        out[i, FP6_PAGE_TOKENS * FP6_ROW_BYTES:] = scales.view(np.uint8)
+    return out
+
+
+def dequantize_rows_fp6(pages6, page_ids, slots) -> np.ndarray:
+    """Stored rows (page_ids[k], slots[k]) of fp6 pages as float64 [k][576]: code value * scale."""
+    pages6 = np.asarray(pages6, dtype=np.uint8)
+    page_ids = np.asarray(page_ids)
+    slots = np.asarray(slots)
+    rows = np.stack([pages6[p, s * FP6_ROW_BYTES:(s + 1) * FP6_ROW_BYTES] for p, s in zip(page_ids, slots)]) \
+        if len(page_ids) else np.zeros((0, FP6_ROW_BYTES), np.uint8)
+    off = FP6_PAGE_TOKENS * FP6_ROW_BYTES
+    scales = np.array([pages6[p, off + 4 * s:off + 4 * s + 4].view(np.float32)[0] for p, s in zip(page_ids, slots)],
+                      dtype=np.float64)
+    return FP6_VALUES[unpack_fp6(rows)] * scales[:, None]
+
+
+def latent_decode_batch_fp6(q_abs, pages6, block_table, seq_lens, scale, d_c=512, batch=None,
+                            heads=None):
+    """The latent-space decode over an fp6 cache: the same attention as latent_decode_batch, on the
+    numbers the cache stores (each row dequantized exactly)."""
+    q_abs = _f64(q_abs)
+    B, H, _ = q_abs.shape
+    o = np.full((B, H, d_c), np.nan)
+    lse = np.full((B, H), np.nan)
+    for b in _sel(B, batch):
+        n = int(seq_lens[b])
+        pg, sl = page_and_slot(block_table, b, np.arange(n), FP6_PAGE_TOKENS)
+        if n and (pg < 0).any():
+            raise ValueError("block table has no page for a token inside the sequence")
+        rows = dequantize_rows_fp6(pages6, pg, sl)
+        for h in _sel(H, heads):
+            o[b, h], lse[b, h], _ = latent_attention(q_abs[b, h], rows, d_c, scale)
+    return o, lse
 
 
 # --------------------------------------------------------------------------------------------------

@@ -394,3 +394,121 @@ def test_latent_row_vs_brute_force():
     rows = O.latent_rows_batch(np.stack([h, -h]), w_dkv, w_kr, [pos, 0], base)
     assert np.allclose(rows[0], row) and np.allclose(rows[1, :4], -np.array(c))
     assert np.allclose(rows[1, 4:], -np.array(k))      # position 0: no rotation
+
+
+# --------------------------------------------------------------------------------------------------
+# The ~6-bit cache: FP6 E2M3 codes with one power-of-two scale per row
+# --------------------------------------------------------------------------------------------------
+
+# The 32 non-negative E2M3 magnitudes as the format lists them (subnormals k/8, then three binades
+# with steps 1/8, 1/4, 1/2), written out by hand rather than from the field formula.
+_E2M3_MAGNITUDES = [0, 0.125, 0.25, 0.375, 0.5, 0.625, 0.75, 0.875,
+                    1.0, 1.125, 1.25, 1.375, 1.5, 1.625, 1.75, 1.875,
+                    2.0, 2.25, 2.5, 2.75, 3.0, 3.25, 3.5, 3.75,
+                    4.0, 4.5, 5.0, 5.5, 6.0, 6.5, 7.0, 7.5]
+
+
+def test_fp6_code_table():
+    """Every code against the format's value list; the sign bit negates (code 32 is -0)."""
+    assert O.FP6_VALUES[:32].tolist() == _E2M3_MAGNITUDES
+    assert (O.FP6_VALUES[32:] == -O.FP6_VALUES[:32]).all()
+    assert math.copysign(1.0, O.fp6_e2m3_value(32)) == -1.0
+    assert O.fp6_e2m3_value(0b011111) == 7.5 and O.fp6_e2m3_value(0b001000) == 1.0
+    assert O.fp6_e2m3_value(0b000001) == 0.125
+
+
+def _grid_round(y):
+    """Rounding by grid spacing, a formulation independent of the oracle's search: steps 1/8 below
+    2, 1/4 below 4, 1/2 above, half to even on the grid index, magnitudes capped at 7.5."""
+    a = min(abs(y), 7.5)
+    step = 0.125 if a < 2 else 0.25 if a < 4 else 0.5
+    k = a / step
+    r = math.floor(k)
+    if k - r > 0.5 or (k - r == 0.5 and r % 2 == 1):
+        r += 1
+    return math.copysign(min(r * step, 7.5), y)
+
+
+def test_fp6_rounding_ties_and_saturation():
+    cases = {0.0625: 0.0, 0.1875: 0.25, 0.9375: 1.0, 1.9375: 2.0, 2.125: 2.0, 3.875: 4.0,
+             6.75: 7.0, 7.25: 7.0, 7.75: 7.5, 100.0: 7.5, 0.3: 0.25, 5.2: 5.0}
+    for y, want in cases.items():
+        for sgn in (1.0, -1.0):
+            got = O.FP6_VALUES[O.fp6_e2m3_round(np.array([sgn * y]))[0]]
+            assert got == sgn * want, (sgn * y, got)
+    assert O.fp6_e2m3_round(np.array([-0.0]))[0] == 32
+
+
+def test_fp6_rounding_against_the_grid():
+    """Random values and every midpoint between neighbouring magnitudes, against _grid_round."""
+    rng = np.random.default_rng(11)
+    mids = [(a + b) / 2 for a, b in zip(_E2M3_MAGNITUDES, _E2M3_MAGNITUDES[1:])]
+    ys = np.concatenate([rng.uniform(-8, 8, 4000), rng.normal(0, 2, 2000), mids, np.negative(mids)])
+    got = O.FP6_VALUES[O.fp6_e2m3_round(ys)]
+    want = np.array([_grid_round(float(y)) for y in ys])
+    assert np.array_equal(got, want)
+
+
+def test_fp6_packing_layout():
+    """Code i at bits 6i .. 6i+5, least significant bit first, bytes little-endian."""
+    assert O.pack_fp6([1, 0, 0, 0]).tolist() == [0x01, 0x00, 0x00]
+    assert O.pack_fp6([0, 1, 0, 0]).tolist() == [0x40, 0x00, 0x00]
+    assert O.pack_fp6([0, 0, 1, 0]).tolist() == [0x00, 0x10, 0x00]
+    assert O.pack_fp6([0, 0, 0, 63]).tolist() == [0x00, 0x00, 0xFC]
+    assert O.pack_fp6([63, 0, 0, 0]).tolist() == [0x3F, 0x00, 0x00]
+    codes = np.random.default_rng(3).integers(0, 64, (5, 576)).astype(np.uint8)
+    packed = O.pack_fp6(codes)
+    assert packed.shape == (5, 432)
+    assert np.array_equal(O.unpack_fp6(packed), codes)
+
+
+def test_fp6_row_exponent():
+    assert O.fp6_row_exponent(7.5) == 0
+    assert O.fp6_row_exponent(7.5 * 2.0 ** -3) == -3
+    assert O.fp6_row_exponent(np.nextafter(7.5, 8.0)) == 1
+    assert O.fp6_row_exponent(3.0) == -1            # 3 <= 3.75 but > 1.875
+    assert O.fp6_row_exponent(0.0) == -126
+    assert O.fp6_row_exponent(1e-40) == -126
+
+
+def test_fp6_quantization_error_bound():
+    """A stored number is within half a grid step (at its binade, times the row scale) of the bf16
+    input, and the row's largest magnitude lands in (3.75, 7.5] times the scale."""
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        x = (rng.normal(0, 1, 576) * 2.0 ** rng.integers(-20, 20)).astype(np.float32)
+        codes, e = O.quantize_row_fp6(x.astype(np.float64))
+        deq = O.FP6_VALUES[codes] * 2.0 ** e
+        y = np.abs(x) / 2.0 ** e
+        step = np.where(y < 2, 0.125, np.where(y < 4, 0.25, 0.5)) * 2.0 ** e
+        assert (np.abs(deq - x) <= step / 2).all()
+        assert 3.75 < np.abs(x).max() / 2.0 ** e <= 7.5
+
+
+def test_fp6_bytes_per_token_matches_the_pages():
+    """432 bytes of codes plus a 4-byte scale per row; over DeepSeek-V2's 60 layers that is 26,160
+    bytes, the "near 26 KB per token" of the audit (within 1 %)."""
+    assert O.FP6_ROW_BYTES == 432
+    per_token = O.mla_numbers_per_token(512, 64, 60) * 6 / 8 + 60 * 4
+    assert per_token == 26160
+    assert abs(per_token - 26000) / 26000 < 0.01
+    assert O.FP6_PAGE_BYTES == 64 * 436
+
+
+def test_fp6_decode_is_attention_on_the_stored_numbers():
+    """The fp6 decode equals the plain latent decode run on the dequantized rows, and a cache whose
+    numbers are already code values times a power of two is stored without loss."""
+    rng = np.random.default_rng(8)
+    pages = 3
+    k = rng.integers(-3, 3, (pages, 64, 1)).astype(np.float64)
+    exact = O.FP6_VALUES[rng.integers(0, 64, (pages, 64, 576))] * 2.0 ** k
+    exact[:, :, 0] = 7.5 * 2.0 ** k[:, :, 0]      # every row's largest magnitude is 7.5 * 2^k
+    bits = (exact.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(O.bf16_to_f64(bits), exact)
+    pages6 = O.quantize_pages_fp6(bits)
+    bt = np.array([[2, 0], [1, -1]], np.int32)
+    lens = np.array([100, 37])
+    q = rng.normal(0, 0.5, (2, 4, 576))
+    o6, l6 = O.latent_decode_batch_fp6(q, pages6, bt, lens, 0.07)
+    o, l = O.latent_decode_batch(q, bits, bt, lens, 0.07)
+    assert np.array_equal(o6, o) and np.array_equal(l6, l)
