@@ -1,9 +1,11 @@
 """MLA decode over a paged latent cache on MI355X (gfx950): a C-ABI HIP library plus this binding.
 
 The entry points carry the C names: mla_cache_append, mla_absorb_q, mla_decode, mla_out_proj,
-mla_decode_workspace_size, and the producer side mla_cache_append_hidden (with its workspace size).
-Importing the package loads libmla.so and fails if it is not built.
+mla_decode_workspace_size, the producer side mla_cache_append_hidden (with its workspace size), and
+the ~6-bit cache: mla_cache_append_fp6, mla_cache_quantize_fp6, mla_decode_fp6 (FP6_PAGE_BYTES per
+page).  Importing the package loads libmla.so and fails if it is not built.
 """
-from ._lib import (MLA_BF16, MLA_F32, MLAError, mla_abi_version, mla_absorb_q,  # noqa: F401
-                   mla_cache_append, mla_cache_append_hidden, mla_cache_append_hidden_workspace_size,
-                   mla_decode, mla_decode_workspace_size, mla_out_proj, mla_status_string, LIB_PATH)
+from ._lib import (FP6_PAGE_BYTES, MLA_BF16, MLA_F32, MLAError, mla_abi_version,  # noqa: F401
+                   mla_absorb_q, mla_cache_append, mla_cache_append_fp6, mla_cache_append_hidden,
+                   mla_cache_append_hidden_workspace_size, mla_cache_quantize_fp6, mla_decode,
+                   mla_decode_fp6, mla_decode_workspace_size, mla_out_proj, mla_status_string, LIB_PATH)

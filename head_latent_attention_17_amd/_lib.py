@@ -20,10 +20,11 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTY
           -7: "MLA_ERR_HIP"}
 EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", "mla_cache_append",
            "mla_absorb_q", "mla_decode", "mla_out_proj", "mla_cache_append_hidden_workspace_size",
-           "mla_cache_append_hidden")
+           "mla_cache_append_hidden", "mla_cache_append_fp6", "mla_cache_quantize_fp6", "mla_decode_fp6")
+FP6_PAGE_BYTES = 27904   # MLA_FP6_PAGE_BYTES: 64 rows of 432 code bytes, then 64 float32 scales
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run head_latent_attention_17_amd.build.build()")
+    raise ImportError(f"{LIB_PATH} is not built; run python head_latent_attention_17_amd/build.py")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -46,6 +47,12 @@ lib.mla_cache_append_hidden_workspace_size.restype = _sz
 lib.mla_cache_append_hidden_workspace_size.argtypes = [_i, _i]
 lib.mla_cache_append_hidden.restype = _i
 lib.mla_cache_append_hidden.argtypes = [_p, _i, _i, _p, _i, _p, _p, _p, _p, _f, _i, _p, _sz, _i, _p]
+lib.mla_cache_append_fp6.restype = _i
+lib.mla_cache_append_fp6.argtypes = [_p, _i, _i, _p, _i, _p, _p, _p, _i, _i, _p]
+lib.mla_cache_quantize_fp6.restype = _i
+lib.mla_cache_quantize_fp6.argtypes = [_p, _p, _i, _i, _p]
+lib.mla_decode_fp6.restype = _i
+lib.mla_decode_fp6.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _p, _sz, _i, _i, _p]
 
 
 class MLAError(RuntimeError):
@@ -122,6 +129,42 @@ def mla_cache_append_hidden(kv_cache, block_table, positions, hidden, w_dkv, w_k
                                        _ptr(hidden), _ptr(w_dkv), _ptr(w_kr), float(rope_base),
                                        positions.shape[0], _ptr(workspace), ws_bytes, _dtype_of(hidden),
                                        _stream(stream)), "mla_cache_append_hidden")
+
+
+def _fp6_pages(kv_cache6) -> int:
+    if kv_cache6.dim() != 2 or kv_cache6.shape[1] != FP6_PAGE_BYTES or kv_cache6.element_size() != 1:
+        raise ValueError(f"a ~6-bit cache is a byte tensor [num_pages][{FP6_PAGE_BYTES}]")
+    return kv_cache6.shape[0]
+
+
+def mla_cache_append_fp6(kv_cache6, block_table, positions, c_new, kpe_new, stream=None):
+    """mla_cache_append into the ~6-bit cache: kv_cache6 uint8 [pages][27904] (in place)."""
+    _dev(kv_cache6, block_table, positions, c_new, kpe_new)
+    _check(lib.mla_cache_append_fp6(_ptr(kv_cache6), _fp6_pages(kv_cache6), 64, _ptr(block_table),
+                                    block_table.shape[1], _ptr(positions), _ptr(c_new), _ptr(kpe_new),
+                                    positions.shape[0], _dtype_of(c_new), _stream(stream)),
+           "mla_cache_append_fp6")
+
+
+def mla_cache_quantize_fp6(kv_cache, kv_cache6, stream=None):
+    """bf16 pages [pages][64][576] -> ~6-bit pages uint8 [pages][27904], page for page."""
+    _dev(kv_cache, kv_cache6)
+    if kv_cache.shape[0] != _fp6_pages(kv_cache6):
+        raise ValueError("kv_cache and kv_cache6 must hold the same number of pages")
+    _check(lib.mla_cache_quantize_fp6(_ptr(kv_cache), _ptr(kv_cache6), kv_cache.shape[0], kv_cache.shape[1],
+                                      _stream(stream)), "mla_cache_quantize_fp6")
+
+
+def mla_decode_fp6(q_abs, kv_cache6, block_table, seq_lens, softmax_scale, o_lat, lse=None,
+                   workspace=None, num_splits=0, stream=None):
+    """mla_decode over the ~6-bit cache kv_cache6 uint8 [pages][27904]; other arguments as mla_decode."""
+    _dev(q_abs, kv_cache6, block_table, seq_lens, o_lat, lse, workspace)
+    B, H = q_abs.shape[0], q_abs.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.mla_decode_fp6(_ptr(q_abs), _ptr(kv_cache6), _fp6_pages(kv_cache6), 64, _ptr(block_table),
+                              block_table.shape[1], _ptr(seq_lens), B, H, float(softmax_scale), _ptr(o_lat),
+                              _ptr(lse), _ptr(workspace), ws_bytes, int(num_splits), _dtype_of(q_abs),
+                              _stream(stream)), "mla_decode_fp6")
 
 
 def mla_absorb_q(q, w_uk, q_abs, stream=None):

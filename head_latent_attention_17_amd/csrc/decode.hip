@@ -409,6 +409,7 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
 hipError_t launch_decode(const DecodeParams& params, bool f32, hipStream_t s) {
   DecodeParams p = params;
   hipError_t e;
+  if (p.fp6 && (f32 || !mfma_supported(p))) return hipErrorNotSupported;  // matrix-core kernel only
   if (f32) {  // debug mode: fp32 everywhere, fp32 pieces
     p.partial_bf16 = 0;
     p.seq_units = nullptr;

@@ -32,6 +32,17 @@
 //   sigma(x) = 2 (x mod 4) + (x / 4) mod 2.
 // With it, the 16 lanes of one row read of the score operand (16 tokens, one chunk) and of one
 // transposing read (4 tokens x 2 chunks) always land on 16 different 16-byte bank groups.
+//
+// ~6-bit cache (FP6 template argument).  Pages hold 6-bit E2M3 codes with one power-of-two scale
+// per row, so every stored number is exactly a bf16 number.  Each wave copies its own rows of a
+// tile (32 / waves rows: codes and scales, 13.6 KB per tile in all) into a wave-private 3-stage
+// LDS ring, three tiles ahead, and converts them with v_cvt_scalef32_pk32_bf16_fp6 (32 codes per
+// instruction, the scale's exponent applied exactly) into the same swizzled bf16 tile layout, two
+// tiles ahead, spread over the output product.  The bf16 ring then has three stages (the tile whose
+// output product runs, the tile whose scores run, the tile being converted) and everything after it
+// is the bf16 path unchanged.  Reading only the codes, the conversion needs no barrier of its own:
+// a wave converts exactly the rows it copied, and the barrier that opens each iteration publishes
+// the converted tile.
 #include "mla_device.h"
 
 namespace mla {
@@ -43,6 +54,8 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(6 * sizeof(unsigned)))) unsigned u32x6;
+typedef __attribute__((__vector_size__(16 * sizeof(unsigned)))) unsigned u32x16;
 #define LDS_AS __attribute__((address_space(3)))
 #define CONST_AS __attribute__((address_space(4)))
 
@@ -72,6 +85,9 @@ __device__ __forceinline__ int tile_offset(int t, int c) {
   const int slot = 8 * (tl ^ (tg & 1)) + (cl ^ sigma(tl));
   return ((tg * kCG + (c >> 3)) * 64 + slot) * 16;
 }
+
+// s_waitcnt lgkmcnt(0) leaving the other counters alone.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
 
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
 template <int N>
@@ -344,6 +360,110 @@ __device__ __forceinline__ bf16x8 v_operand(unsigned tv, int db, int m) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// ---- ~6-bit cache ---------------------------------------------------------------------------------
+// Per wave and tile: rows R w .. R w + R - 1 (R = 32 / waves), copied as their contiguous codes
+// (432 bytes a row, every 16-byte piece inside one row) then their R scales; converted as units of
+// 32 codes (24 bytes) each, 18 to a row.
+template <int NW>
+struct Fp6Geom {
+  static constexpr int kRows = kTileTok / NW;
+  static constexpr int kDataBytes = kRows * kFp6RowBytes;            // 3,456 / 6,912 / 13,824
+  static constexpr int kDataCopies = (kDataBytes + 1023) / 1024;     // 4 / 7 / 14, the last partial
+  static constexpr int kCopies = kDataCopies + 1;                    // plus one for the scales
+  static constexpr int kWaveBytes = kDataBytes + kRows * 4;
+  static constexpr int kUnits = kRows * (kRow / 32);                 // 144 / 288 / 576
+  static constexpr int kRounds = (kUnits + 63) / 64;                 // 3 / 5 / 9
+  // Rounds inside the 32 steps of the output product, from step 4: loaded at 4 + kRoundStep k,
+  // converted and stored two steps later, one unit in flight at a time.
+  static constexpr int kRoundStep = 28 / kRounds > 8 ? 8 : 28 / kRounds;   // 8 / 5 / 3
+  static_assert(kRoundStep >= 3 && 4 + kRoundStep * (kRounds - 1) + 2 < 32, "rounds fit the product");
+};
+constexpr int kFp6Stages = 3;
+
+// One 4-byte-per-lane copy HBM -> LDS: lane l's dword from gbase + voff lands at LDS byte lds + 4 l.
+__device__ __forceinline__ void dma4(const char* gbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// This wave's copies of one tile (tile rows start at page slot slot0, nt valid rows) into its
+// region `lds` of an fp6 stage.  A ragged tile repeats its last valid row for the missing ones, so
+// every converted number is finite.  Always kCopies instructions, each with some lane active.
+template <int NW>
+__device__ __forceinline__ void issue_tile6(const char* page_base, int slot0, int nt, unsigned lds, int wave) {
+  using G = Fp6Geom<NW>;
+  const int ln = lane_id();
+  const int r0 = wave * G::kRows;
+#pragma unroll
+  for (int j = 0; j < G::kDataCopies; ++j) {
+    const int o = 1024 * j + 16 * ln;
+    if (j < G::kDataCopies - 1 || o < G::kDataBytes) {
+      const int r = o / kFp6RowBytes;
+      const int rr = min(r0 + r, nt - 1);
+      dma16(page_base, (unsigned)((slot0 + rr) * kFp6RowBytes + (o - r * kFp6RowBytes)), lds + 1024 * j);
+    }
+  }
+  if (ln < G::kRows)
+    dma4(page_base, (unsigned)(kPage * kFp6RowBytes + 4 * (slot0 + min(r0 + ln, nt - 1))), lds + G::kDataBytes);
+}
+
+// One conversion unit in flight: 32 codes and the row scale.
+struct Fp6Unit {
+  u32x6 codes;
+  float scale;
+};
+
+// Loads unit u of this wave's rows from its fp6 region (unit u: row u / 18, codes 32 (u % 18) ..).
+// Units are numbered lane + 64 k for round k, the lane taken from lane_id() so that the address
+// arithmetic stays where it is used instead of holding registers across the tile loop.
+template <int NW>
+__device__ __forceinline__ Fp6Unit fp6_load(unsigned region, int k) {
+  using G = Fp6Geom<NW>;
+  const int u = lane_id() + 64 * k;
+  const int r = u / (kRow / 32), g = u - r * (kRow / 32);
+  const LDS_AS char* src = (const LDS_AS char*)(uintptr_t)region + r * kFp6RowBytes + 24 * g;
+  const u32x2 a = *reinterpret_cast<const LDS_AS u32x2*>(src);
+  const u32x2 b = *reinterpret_cast<const LDS_AS u32x2*>(src + 8);
+  const u32x2 c = *reinterpret_cast<const LDS_AS u32x2*>(src + 16);
+  Fp6Unit x;
+  x.codes = u32x6{a[0], a[1], b[0], b[1], c[0], c[1]};
+  x.scale = *reinterpret_cast<const LDS_AS float*>((const LDS_AS char*)(uintptr_t)region + G::kDataBytes + 4 * r);
+  return x;
+}
+
+// Converts a unit (only the scale's exponent is applied, so code * 2^e exactly) and writes its 32
+// bf16 numbers, chunks 4 g .. 4 g + 3 of its row, into the swizzled bf16 tile at `stage` (1 KB
+// aligned).  Those four chunks share a block and differ only in the two low chunk bits, which the
+// swizzle XORs with a row constant: chunk 4 g + j sits at the offset of chunk 4 g XOR 16 j.  The
+// conversion is written as asm: the compiler's builtin for it returned its first element in every
+// position.
+template <int NW>
+__device__ __forceinline__ void fp6_store(const Fp6Unit& x, int k, unsigned stage, int wave) {
+  using G = Fp6Geom<NW>;
+  u32x16 v;
+  asm("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2" : "=&v"(v) : "v"(x.codes), "v"(x.scale));
+  const int u = lane_id() + 64 * k;
+  const int r = u / (kRow / 32), g = u - r * (kRow / 32);
+  const unsigned a0 = stage + (unsigned)tile_offset(wave * G::kRows + r, 4 * g);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<LDS_AS u32x4*>((LDS_AS char*)(uintptr_t)(a0 ^ (16u * j))) =
+        u32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+}
+
+// Whole-tile conversion (prologue): every unit of this wave's rows.
+template <int NW>
+__device__ __forceinline__ void fp6_convert_all(unsigned region, unsigned stage, int wave) {
+  using G = Fp6Geom<NW>;
+  const int ln = lane_id();
+#pragma unroll
+  for (int k = 0; k < G::kRounds; ++k) {
+    if (ln + 64 * k < G::kUnits) fp6_store<NW>(fp6_load<NW>(region, k), k, stage, wave);
+  }
+}
+
 // Workgroups go to the eight XCDs round-robin (workgroup i to XCD i mod 8), each XCD with its own
 // L2.  Consecutive work units, which hold neighbouring pages and mostly the same sequence, are
 // placed on one XCD so that they share its L2 for that sequence's query and block-table lines.
@@ -352,13 +472,17 @@ __device__ __forceinline__ int xcd_unit(int id, int n) {
   return x * per + min(x, rem) + id / 8;
 }
 
-template <int NW>
+template <int NW, bool FP6>
 __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p) {
   constexpr int kPer = kBlocks / NW;  // copies per wave per tile
-  __shared__ __attribute__((aligned(1024))) char ring[kStages][kTileBytes];
+  using G6 = Fp6Geom<NW>;
+  __shared__ __attribute__((aligned(1024))) char ring[FP6 ? 3 : kStages][kTileBytes];
   // Target of the copies a four-wave unit issues after its last tile: they keep the count of copies
   // per tile fixed, which the counted waits rely on, and nothing reads them.
-  __shared__ __attribute__((aligned(1024))) char sink[NW == 4 ? kPer * 1024 : 16];
+  __shared__ __attribute__((aligned(1024))) char sink[(!FP6 && NW == 4) ? kPer * 1024 : 16];
+  // ~6-bit cache: the waves' private copy regions, three tiles' worth.
+  __shared__ __attribute__((aligned(16))) char ring6[FP6 ? kFp6Stages * NW * G6::kWaveBytes : 16];
+  auto stg = [](int t) __attribute__((always_inline)) { return FP6 ? t % 3 : stage_of(t); };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -394,23 +518,58 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
 
   // Prologue: three tiles in flight.
   int issued = 0;
+  // ~6-bit cache: this wave's fp6 region for tile t, and the copies of the tile at cursor `ld`
+  const unsigned r6 = (unsigned)(uintptr_t)(LDS_AS char*)ring6 + wave * G6::kWaveBytes;
+  auto region6 = [&](int t) __attribute__((always_inline)) {
+    return r6 + (unsigned)((t % kFp6Stages) * NW * G6::kWaveBytes);
+  };
+  auto issue6 = [&](int page) __attribute__((always_inline)) {
+    const char* pb = reinterpret_cast<const char*>(p.cache) + (size_t)page * kFp6PageBytes;
+    issue_tile6<NW>(pb, (int)((unsigned)ld.t % kPage), min(kTileTok, ld.t_end - ld.t), region6(issued), wave);
+    ld.advance();
+    ++issued;
+  };
+  if constexpr (FP6) {
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    if (ld.valid) {
-      issue_tile<NW>(p, ld, (LDS_AS char*)ring[s], wave);
-      ld.advance();
-      ++issued;
+    for (int s = 0; s < kFp6Stages; ++s) {
+      if (ld.valid) issue6(ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage));
     }
+    // Tiles 0 and 1 are converted here, the rest two tiles ahead inside the loop.  Loads complete in
+    // issue order, so the query has landed once tile 0 has.
+    constexpr int C = G6::kCopies;
+    if (issued >= 3) wait_vmcnt<2 * C>();
+    else if (issued == 2) wait_vmcnt<C>();
+    else wait_vmcnt<0>();
+    fp6_convert_all<NW>(region6(0), (unsigned)(uintptr_t)(LDS_AS char*)ring[0], wave);
+    if (issued >= 2) {
+      if (issued >= 3) wait_vmcnt<C>();
+      else wait_vmcnt<0>();
+      fp6_convert_all<NW>(region6(1), (unsigned)(uintptr_t)(LDS_AS char*)ring[1], wave);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) {
+      if (ld.valid) {
+        issue_tile<NW>(p, ld, (LDS_AS char*)ring[s], wave);
+        ld.advance();
+        ++issued;
+      }
+    }
+    // Loads complete in issue order: with at most the prologue's copies outstanding (capped at the
+    // counter's 63, which only waits for more), the query has landed.
+    if (issued >= 3) wait_vmcnt<(3 * kPer < 63 ? 3 * kPer : 63)>();
+    else if (issued == 2) wait_vmcnt<(2 * kPer < 63 ? 2 * kPer : 63)>();
+    else wait_vmcnt<(kPer < 63 ? kPer : 63)>();
   }
-  // Loads complete in issue order: with at most the prologue's copies outstanding (capped at the
-  // counter's 63, which only waits for more), the query has landed.
-  if (issued >= 3) wait_vmcnt<(3 * kPer < 63 ? 3 * kPer : 63)>();
-  else if (issued == 2) wait_vmcnt<(2 * kPer < 63 ? 2 * kPer : 63)>();
-  else wait_vmcnt<(kPer < 63 ? kPer : 63)>();
   // Waits until the copies of tile `t` (this wave's part) have landed, then for every wave.
   // Vector loads complete in issue order: it is enough to let the tiles issued after it stay in
   // flight.
   auto tile_ready = [&](int t) __attribute__((always_inline)) {
+    if constexpr (FP6) {  // the tile was converted by every wave: their LDS writes, then the barrier
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+      return;
+    }
     const int younger = issued - t - 1;
     if (younger >= 2) wait_vmcnt<(2 * kPer < 63 ? 2 * kPer : 63)>();
     else if (younger == 1) wait_vmcnt<(kPer < 63 ? kPer : 63)>();
@@ -420,7 +579,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   // Refills the stage of the tile before `t` (every wave is past it) with the next tile.
   auto refill = [&](int t) __attribute__((always_inline)) {
     if (ld.valid) {
-      issue_tile<NW>(p, ld, (LDS_AS char*)ring[stage_of(t + kStages - 1)], wave);
+      issue_tile<NW>(p, ld, (LDS_AS char*)ring[stg(t + kStages - 1)], wave);
       ld.advance();
       ++issued;
     }
@@ -469,7 +628,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     f32x16 s_cur;
     {
       tile_ready(it);
-      const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it)] + k_off;
+      const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stg(it)] + k_off;
       bf16x8 ka[kKAhead + 1];
 #pragma unroll
       for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tk, ks);
@@ -494,11 +653,22 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // repeats its last row in place of the missing ones; after the unit's last tile the copies
       // go to the sink (from the first page, which always exists).  The addresses are worked out
       // before the wait below, so that the block-table read overlaps it; the copies start after it.
+      // The ~6-bit cache copies a twelfth of the bytes per wave and issues them all at once.
       const char* sp_base = reinterpret_cast<const char*>(p.cache);
       unsigned sp_lane = 0, sp_lds = 0;
       int sp_page = 0, sp_tok = 0;
       bool sp_have = false;
-      if constexpr (NW == 4) {
+      if constexpr (FP6) {
+        // The converted tile it + 1 is published by the barrier; the block-table read for the
+        // copies of tile it + 3 is issued after this wave's own LDS writes are done, so that it
+        // overlaps the barrier instead of being waited for before it.
+        wait_lgkmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
+        sp_have = ld.valid;
+        if (ld.valid) sp_page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage);
+        __builtin_amdgcn_s_barrier();
+        if (sp_have) issue6(sp_page);
+      } else if constexpr (NW == 4) {
         const int ln = lane_id();
         const int tl = (ln >> 3) ^ (wave & 1);
         const unsigned cl16 = (unsigned)((ln & 7) ^ sigma(tl)) * 16u;
@@ -517,16 +687,18 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       }
       // The next tile must be in LDS before its scores start; the barrier also frees the stage of
       // tile it - 1.
-      tile_ready(last ? it : it + 1);
-      if constexpr (NW == 4) {
-        ++issued;
-        asm volatile("" : "+s"(sp_page));  // the page is first needed here, behind the wait
-        if (sp_have) sp_base += ((size_t)sp_page * kPage + sp_tok) * (kRow * 2);
-      } else {
-        refill(it);
+      if constexpr (!FP6) {
+        tile_ready(last ? it : it + 1);
+        if constexpr (NW == 4) {
+          ++issued;
+          asm volatile("" : "+s"(sp_page));  // the page is first needed here, behind the wait
+          if (sp_have) sp_base += ((size_t)sp_page * kPage + sp_tok) * (kRow * 2);
+        } else {
+          refill(it);
+        }
       }
       auto spread_copy = [&](int j) __attribute__((always_inline)) {
-        if constexpr (NW == 4) dma16_group(sp_base, sp_lane, sp_lds, j);
+        if constexpr (NW == 4 && !FP6) dma16_group(sp_base, sp_lane, sp_lds, j);
       };
 
       // ---- softmax of tile it (base 2), lane = head, registers = tokens, spread over the next
@@ -570,7 +742,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       f32x16 s_nxt;
       if (!last) {
         // scores of tile it + 1 into s_nxt, one softmax step of tile it after each MFMA
-        const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it + 1)] + k_off;
+        const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stg(it + 1)] + k_off;
         bf16x8 ka[kKAhead + 1];
 #pragma unroll
         for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tk, ks);
@@ -630,7 +802,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // then those of pb1 (the exponents of pb1 are computed during the first pass); operands
       // kVAhead MFMAs ahead.
       {
-        const unsigned tv = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it)] + v_off;
+        const unsigned tv = (unsigned)(uintptr_t)(LDS_AS char*)ring[stg(it)] + v_off;
+        // ~6-bit cache: tile it + 2 is converted here, its stage free since the barrier above
+        const bool conv = FP6 && it + 2 < issued;
+        const unsigned cv_src = FP6 ? region6(it + 2) : 0u;
+        const unsigned cv_dst = FP6 ? (unsigned)(uintptr_t)(LDS_AS char*)ring[stg(it + 2)] : 0u;
+        Fp6Unit cbuf;
         bf16x8 va[kVAhead + 1];
 #pragma unroll
         for (int i = 0; i < kVAhead; ++i) va[i] = v_operand(tv, i & 15, i >> 4);
@@ -644,6 +821,21 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
           else mfma_a_nw(o[i & 15], va[i % (kVAhead + 1)], pb1);
           if (i < 8) softmax_exp(8 + i);
           if (i == 8) l_sum += ls0 + ls1;
+          if constexpr (FP6) {
+            if (conv) {
+              if (i == 4) {  // this wave's copies of tile it + 2 have landed (tile it + 3's may not)
+                if (it + 3 < issued) wait_vmcnt<G6::kCopies>();
+                else wait_vmcnt<0>();
+              }
+#pragma unroll
+              for (int k = 0; k < G6::kRounds; ++k) {
+                const int at = 4 + k * G6::kRoundStep;
+                const bool mine = lane + 64 * k < G6::kUnits;
+                if (i == at && mine) cbuf = fp6_load<NW>(cv_src, k);
+                if (i == at + 2 && mine) fp6_store<NW>(cbuf, k, cv_dst, wave);
+              }
+            }
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -674,7 +866,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // conflicts, and passes its rows through it a quarter at a time.
       constexpr int kPad = 256 + 16;
       __builtin_amdgcn_s_barrier();
-      LDS_AS char* region = (LDS_AS char*)ring[stage_of(it - 1)] + wave * 32 * kPad;
+      LDS_AS char* region = (LDS_AS char*)ring[stg(it - 1)] + wave * 32 * kPad;
       const int hw = ln & 31, hl = ln >> 5;
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
@@ -711,10 +903,20 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
 bool mfma_supported(const DecodeParams& p) { return p.heads == 128 || p.heads == 64 || p.heads == 32; }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
+  if (p.fp6) {
+    // No one-wave variant: with its conversion the compiler keeps that kernel's output accumulators
+    // in memory across the tile loop, which the unpadded MFMA wrappers above do not allow.
+    switch (p.heads) {
+      case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, true>), dim3(p.num_units), dim3(256), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, true>), dim3(p.num_units), dim3(128), 0, s, p); break;
+      default: return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+  }
   switch (p.heads) {
-    case 128: hipLaunchKernelGGL(decode_mfma_kernel<4>, dim3(p.num_units), dim3(256), 0, s, p); break;
-    case 64: hipLaunchKernelGGL(decode_mfma_kernel<2>, dim3(p.num_units), dim3(128), 0, s, p); break;
-    case 32: hipLaunchKernelGGL(decode_mfma_kernel<1>, dim3(p.num_units), dim3(64), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false>), dim3(p.num_units), dim3(256), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false>), dim3(p.num_units), dim3(128), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<1, false>), dim3(p.num_units), dim3(64), 0, s, p); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

@@ -51,14 +51,14 @@ const char* mla_status_string(int status) {
     case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: invalid or inconsistent size";
     case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown dtype";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
-    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: page_size must be 64, heads in {16,32,64,128}";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: page_size must be 64, heads in {16,32,64,128} (64 or 128 and bf16 for the ~6-bit cache)";
     case MLA_ERR_BLOCK_TABLE: return "MLA_ERR_BLOCK_TABLE: block table entry out of range";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch failed";
     default: return "unknown mla_status";
   }
 }
 
-int mla_abi_version(void) { return 101; }
+int mla_abi_version(void) { return 102; }
 
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype) {
@@ -141,14 +141,15 @@ mla_status mla_out_proj(const void* o_lat, const void* w_uv, void* out, int batc
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
-                      const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
-                      int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
-                      void* workspace, size_t workspace_bytes_given, int num_splits, mla_dtype dtype,
-                      hipStream_t stream) {
+static mla_status decode_common(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                                const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                                int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
+                                void* workspace, size_t workspace_bytes_given, int num_splits, mla_dtype dtype,
+                                bool fp6, hipStream_t stream) {
   if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
   if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
   if (!valid_heads(num_heads)) return MLA_ERR_UNSUPPORTED;
+  if (fp6 && (dtype != MLA_BF16 || num_heads < 64)) return MLA_ERR_UNSUPPORTED;
   if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1 || num_splits < 0) return MLA_ERR_SHAPE;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
@@ -173,6 +174,7 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
   p.ws_o = static_cast<float*>(workspace);
   p.ws_ml = p.ws_o + ((size_t)units + batch) * num_heads * kDc;
   p.seq_units = reinterpret_cast<int*>(p.ws_ml + ((size_t)units + batch) * num_heads * 2);
+  p.fp6 = fp6 ? 1 : 0;
   p.num_pages = num_pages;
   p.max_blocks = max_blocks_per_seq;
   p.batch = batch;
@@ -181,6 +183,56 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.partial_bf16 = 0;  // chosen with the kernel in launch_decode
   hipError_t e = launch_decode(p, dtype == MLA_F32, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                      const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                      int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
+                      void* workspace, size_t workspace_bytes_given, int num_splits, mla_dtype dtype,
+                      hipStream_t stream) {
+  return decode_common(q_abs, kv_cache, num_pages, page_size, block_table, max_blocks_per_seq, seq_lens, batch,
+                       num_heads, softmax_scale, o_lat, lse, workspace, workspace_bytes_given, num_splits, dtype,
+                       false, stream);
+}
+
+mla_status mla_decode_fp6(const void* q_abs, const void* kv_cache6, int num_pages, int page_size,
+                          const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                          int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
+                          void* workspace, size_t workspace_bytes_given, int num_splits, mla_dtype dtype,
+                          hipStream_t stream) {
+  return decode_common(q_abs, kv_cache6, num_pages, page_size, block_table, max_blocks_per_seq, seq_lens, batch,
+                       num_heads, softmax_scale, o_lat, lse, workspace, workspace_bytes_given, num_splits, dtype,
+                       true, stream);
+}
+
+mla_status mla_cache_append_fp6(void* kv_cache6, int num_pages, int page_size, const int32_t* block_table,
+                                int max_blocks_per_seq, const int32_t* positions, const void* c_new,
+                                const void* kpe_new, int batch, mla_dtype dtype, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (num_pages < 1) return MLA_ERR_SHAPE;
+  if (!kv_cache6 || !block_table || !positions || !c_new || !kpe_new) return MLA_ERR_NULL;
+  if (debug_checks_enabled()) {
+    bool bad = false;
+    if (check_tables(block_table, max_blocks_per_seq, positions, batch, num_pages, true, stream, &bad) != hipSuccess)
+      return MLA_ERR_HIP;
+    if (bad) return MLA_ERR_BLOCK_TABLE;
+  }
+  hipError_t e = launch_append_fp6(kv_cache6, block_table, max_blocks_per_seq, positions, c_new, kpe_new, batch,
+                                   dtype == MLA_F32, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_cache_quantize_fp6(const void* kv_cache, void* kv_cache6, int num_pages, int page_size,
+                                  hipStream_t stream) {
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (num_pages < 0) return MLA_ERR_SHAPE;
+  if (num_pages == 0) return MLA_OK;
+  if (!kv_cache || !kv_cache6) return MLA_ERR_NULL;
+  hipError_t e = launch_quantize_pages_fp6(kv_cache, kv_cache6, num_pages, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

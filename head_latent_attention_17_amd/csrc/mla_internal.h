@@ -16,6 +16,8 @@ constexpr int kQdim = 192;    // [q_nope | q_pe]
 constexpr int kPage = 64;     // tokens per page
 constexpr int kNumCUs = 256;  // MI355X compute units (used only to pick the automatic split)
 constexpr int kAppendChunks = 20;  // 5,120 / 256: partial sums per output of the producer products
+constexpr int kFp6RowBytes = kRow * 6 / 8;                       // 432: a row of 6-bit codes
+constexpr int kFp6PageBytes = kPage * kFp6RowBytes + kPage * 4;  // 27,904: rows, then fp32 scales
 
 // Everything a decode launch needs.  Pointers are device pointers.
 struct DecodeParams {
@@ -32,6 +34,7 @@ struct DecodeParams {
                        // derive the unit range from seq_lens)
   int partial_bf16;    // 0: fp32 un-normalised sums; 1: bf16 sums already divided by the
                        // softmax sum, in the first half of each slot (set by launch_decode)
+  int fp6;            // 1: cache holds ~6-bit pages (kFp6PageBytes each), 0: bf16 rows
   int num_pages;
   int max_blocks;
   int batch;
@@ -59,6 +62,11 @@ hipError_t launch_append_hidden(void* cache, const int32_t* block_table, int max
                                 const void* w_kr, double rope_base, int batch, float* part, bool f32,
                                 hipStream_t s);
 size_t append_hidden_workspace_bytes(int batch);
+// ~6-bit cache: quantize and write one row per sequence; quantize whole bf16 pages.
+hipError_t launch_append_fp6(void* cache, const int32_t* block_table, int max_blocks,
+                             const int32_t* positions, const void* c_new, const void* kpe_new, int batch,
+                             bool f32, hipStream_t s);
+hipError_t launch_quantize_pages_fp6(const void* src, void* dst, int num_pages, hipStream_t s);
 
 // Device-side check of block-table entries and lengths (append = false) or append positions
 // (append = true); synchronises s.  *bad is set when an entry is out of range.

@@ -153,6 +153,49 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
                       hipStream_t stream);
 
 /*
+ * The ~6-bit cache (explainer, the audit after Step 8: deployed V2 keeps each cached number in about
+ * six bits, near 26 KB per token over its 60 layers).  The pages give no format; the reading here:
+ * every number is an FP6 E2M3 code (1 sign, 2 exponent bits with bias 1, 3 mantissa bits; magnitudes
+ * 0, 1/8 .. 7/8, 1 .. 7.5; no infinity or NaN), rounded to nearest with ties to the even code, and
+ * every row carries one scale 2^e, e the smallest integer >= -126 with the row's largest magnitude
+ * at most 7.5 * 2^e.  A stored number is code_value * 2^e exactly.
+ *   kv_cache6  uint8 [num_pages][MLA_FP6_PAGE_BYTES]: 64 rows of 432 bytes (code i of a row at bits
+ *              6i .. 6i+5 of the row's little-endian bit string), then the 64 scales as float32.
+ * Rows must hold finite values below 2^127 in magnitude.  436 bytes per token and layer, 37.8 % of
+ * the bf16 row.
+ */
+#define MLA_FP6_PAGE_BYTES 27904
+
+/*
+ * mla_cache_append for the ~6-bit cache: row [c_new[b] | kpe_new[b]] is quantized as above and
+ * written to logical position positions[b] of sequence b (codes and scale).  Arguments, dtypes and
+ * errors as mla_cache_append.
+ */
+mla_status mla_cache_append_fp6(void* kv_cache6, int num_pages, int page_size, const int32_t* block_table,
+                                int max_blocks_per_seq, const int32_t* positions, const void* c_new,
+                                const void* kpe_new, int batch, mla_dtype dtype, hipStream_t stream);
+
+/*
+ * Quantizes every row of bf16 pages kv_cache [num_pages][64][576] into kv_cache6 [num_pages]
+ * [MLA_FP6_PAGE_BYTES] (page i to page i, every slot, used or not).  MLA_ERR_UNSUPPORTED unless
+ * page_size is 64; MLA_ERR_SHAPE for num_pages < 0; MLA_ERR_NULL for a null pointer.
+ */
+mla_status mla_cache_quantize_fp6(const void* kv_cache, void* kv_cache6, int num_pages, int page_size,
+                                  hipStream_t stream);
+
+/*
+ * mla_decode over the ~6-bit cache: the same attention on the numbers the cache stores (each row
+ * code_value * 2^e, converted to bf16 exactly inside the kernel).  Arguments, workspace, results
+ * and errors as mla_decode, with two limits: dtype must be MLA_BF16 and num_heads 64 or 128
+ * (MLA_ERR_UNSUPPORTED otherwise).
+ */
+mla_status mla_decode_fp6(const void* q_abs, const void* kv_cache6, int num_pages, int page_size,
+                          const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                          int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
+                          void* workspace, size_t workspace_bytes, int num_splits, mla_dtype dtype,
+                          hipStream_t stream);
+
+/*
  * Per-head value up-projection after the weighted sum (explainer Step 6: W_UV is applied on the
  * output side instead of to every cached token):
  *   out[b][h][:] = o_lat[b][h][:] @ W_UV[h]      (512 -> 128, fp32 accumulation)

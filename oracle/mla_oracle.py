@@ -304,15 +304,15 @@ FP6_VALUES = np.array([fp6_e2m3_value(c) for c in range(64)])
 def fp6_e2m3_round(y) -> np.ndarray:
     """Codes of the E2M3 numbers nearest to y (float64 array): ties go to the code with an even
     mantissa, magnitudes beyond 7.5 saturate to 7.5, and the sign is kept (also for zero).  Written
-    as a search over the 32 magnitudes, not as bit arithmetic."""
+    as a search among the 32 magnitudes (the two neighbours of |y| in the sorted table), not as bit
+    arithmetic."""
     y = np.asarray(y, dtype=np.float64)
     mags = FP6_VALUES[:32]                      # codes 0 .. 31, increasing magnitudes
     a = np.minimum(np.abs(y), FP6_MAX)
-    dist = np.abs(a[..., None] - mags)
-    best = dist.min(axis=-1, keepdims=True)
-    tied = dist == best                         # one or two neighbouring codes
-    even = tied & (np.arange(32) % 2 == 0)
-    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(tied, axis=-1))
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 1, 31)   # mags[hi - 1] < a <= mags[hi]
+    lo = hi - 1
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
     return (code | np.where(np.signbit(y), 32, 0)).astype(np.uint8)
 
 
@@ -322,6 +322,19 @@ def fp6_row_exponent(amax: float) -> int:
     e = FP6_MIN_EXP
     while amax > FP6_MAX * 2.0 ** e:
         e += 1
+    return e
+
+
+def fp6_row_exponents(amax) -> np.ndarray:
+    """fp6_row_exponent for many rows at once: a guess from log2, then corrected with the same exact
+    comparisons (amax <= 7.5 * 2^e, and not for e - 1)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        e = np.ceil(np.log2(np.maximum(amax, 1e-300) / FP6_MAX))
+    e = np.clip(e, FP6_MIN_EXP, 200).astype(np.int64)
+    for _ in range(2):
+        e = np.where(amax > FP6_MAX * np.exp2(e.astype(np.float64)), e + 1, e)
+        e = np.where((e > FP6_MIN_EXP) & (amax <= FP6_MAX * np.exp2(e - 1.0)), e - 1, e)
     return e
 
 
@@ -352,17 +365,18 @@ def unpack_fp6(data) -> np.ndarray:
 
 def quantize_pages_fp6(pages) -> np.ndarray:
     """bf16 pages [n][64][576] -> fp6 pages [n][27904] bytes: 64 packed rows of 432 bytes, then the
-    64 row scales 2^e as little-endian float32."""
+    64 row scales 2^e as little-endian float32.  Each row as quantize_row_fp6, many rows at once."""
     pages = np.asarray(pages)
     n = pages.shape[0]
     out = np.zeros((n, FP6_PAGE_BYTES), np.uint8)
-    for i in range(n):
-        scales = np.empty(FP6_PAGE_TOKENS, np.float32)
-        for t in range(FP6_PAGE_TOKENS):
-            codes, e = quantize_row_fp6(pages[i, t])
-            out[i, t * FP6_ROW_BYTES:(t + 1) * FP6_ROW_BYTES] = pack_fp6(codes)
-            scales[t] = 2.0 ** e
-        out[i, FP6_PAGE_TOKENS * FP6_ROW_BYTES:] = scales.view(np.uint8)
+    for i0 in range(0, n, 64):
+        x = _f64(pages[i0:i0 + 64])                                  # [k][64][576]
+        e = fp6_row_exponents(np.abs(x).max(axis=2))                 # [k][64]
+        codes = fp6_e2m3_round(x / np.exp2(e.astype(np.float64))[..., None])
+        k = x.shape[0]
+        out[i0:i0 + k, :FP6_PAGE_TOKENS * FP6_ROW_BYTES] = pack_fp6(codes).reshape(k, -1)
+        out[i0:i0 + k, FP6_PAGE_TOKENS * FP6_ROW_BYTES:] = \
+            np.exp2(e.astype(np.float64)).astype(np.float32).view(np.uint8).reshape(k, -1)
     return out
 
 

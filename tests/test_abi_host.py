@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.mla_abi_version() == 101
+    assert L.mla_abi_version() == 102
     for code, name in L.STATUS.items():
         assert L.mla_status_string(code).startswith(name)
     assert "unknown" in L.mla_status_string(12345)
@@ -141,3 +141,41 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros(4, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         L.mla_out_proj(x, x, x)
+
+
+def test_fp6_cache_validation():
+    """The ~6-bit cache entry points reject bad arguments before any launch: decode only with bf16
+    activations and 64 or 128 heads; quantize and append with the same checks as the bf16 ones."""
+    L = _lib()
+    assert L.FP6_PAGE_BYTES == 64 * 432 + 64 * 4
+
+    def dec6(**kw):
+        a = dict(q_abs=FAKE, cache=FAKE, num_pages=16, page_size=64, bt=FAKE, max_blocks=16, lens=FAKE,
+                 batch=1, heads=128, scale=0.07, o_lat=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30,
+                 splits=0, dtype=0)
+        a.update(kw)
+        return L.lib.mla_decode_fp6(a["q_abs"], a["cache"], a["num_pages"], a["page_size"], a["bt"],
+                                    a["max_blocks"], a["lens"], a["batch"], a["heads"], a["scale"],
+                                    a["o_lat"], a["lse"], a["ws"], a["ws_bytes"], a["splits"], a["dtype"], None)
+
+    assert dec6(dtype=1) == -5            # fp32 debug mode has no ~6-bit path
+    assert dec6(heads=16) == -5
+    assert dec6(heads=32) == -5
+    assert dec6(heads=100) == -5
+    assert dec6(dtype=7) == -3
+    assert dec6(page_size=32) == -5
+    assert dec6(cache=None) == -1
+    assert dec6(ws_bytes=10) == -4
+    assert dec6(scale=-1.0) == -2
+    assert dec6(batch=0, cache=None, ws=None) == 0
+    q = L.lib.mla_cache_quantize_fp6
+    assert q(FAKE, FAKE, 4, 32, None) == -5
+    assert q(FAKE, FAKE, -1, 64, None) == -2
+    assert q(None, FAKE, 4, 64, None) == -1
+    assert q(None, None, 0, 64, None) == 0
+    a = L.lib.mla_cache_append_fp6
+    assert a(FAKE, 8, 16, FAKE, 1, FAKE, FAKE, FAKE, 2, 0, None) == -5
+    assert a(FAKE, 8, 64, FAKE, 1, None, FAKE, FAKE, 2, 0, None) == -1
+    assert a(FAKE, 0, 64, FAKE, 1, FAKE, FAKE, FAKE, 2, 0, None) == -2
+    assert a(FAKE, 8, 64, FAKE, 1, FAKE, FAKE, FAKE, 2, 5, None) == -3
+    assert a(None, 0, 64, None, 1, None, None, None, 0, 0, None) == 0

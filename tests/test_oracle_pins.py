@@ -512,3 +512,19 @@ def test_fp6_decode_is_attention_on_the_stored_numbers():
     o6, l6 = O.latent_decode_batch_fp6(q, pages6, bt, lens, 0.07)
     o, l = O.latent_decode_batch(q, bits, bt, lens, 0.07)
     assert np.array_equal(o6, o) and np.array_equal(l6, l)
+
+
+def test_fp6_many_rows_match_one_row():
+    """The batched page quantizer and exponent agree with the one-row definitions."""
+    rng = np.random.default_rng(12)
+    amax = np.concatenate([[0.0, 1e-45, 7.5, np.nextafter(7.5, 8), 3.75, np.nextafter(3.75, 0)],
+                           np.exp2(rng.uniform(-140, 120, 3000)), 7.5 * np.exp2(rng.integers(-126, 120, 500))])
+    assert np.array_equal(O.fp6_row_exponents(amax), [O.fp6_row_exponent(float(a)) for a in amax])
+    x = (rng.normal(0, 1, (2, 64, 576)) * np.exp2(rng.integers(-30, 30, (2, 64, 1)))).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    pages6 = O.quantize_pages_fp6(bits)
+    for p in range(2):
+        for t in (0, 17, 63):
+            codes, e = O.quantize_row_fp6(bits[p, t])
+            assert np.array_equal(O.unpack_fp6(pages6[p, t * 432:(t + 1) * 432]), codes)
+            assert pages6[p, 27648 + 4 * t:27648 + 4 * t + 4].view(np.float32)[0] == 2.0 ** e
