@@ -11,6 +11,9 @@ Prints one JSON line.  `value` is latent-cache GB/s over the whole step (tokens 
 time), from K steps timed between two synchronisations with nothing else on the stream.
 `roofline` reports the dominant call, mla_decode, timed with HIP events on the launch stream in a
 second pass of the same K steps.
+`producer` (workloads that append) times mla_cache_append_hidden, the producer side of the cache,
+graph-replayed over 48 weight copies.  `fp6` times mla_decode_fp6 over the ~6-bit form of the same
+cache (FP6 codes and a power-of-two scale per row, 436 bytes per token).
 `cpu_baseline` times the CPU oracle (decompressed form, float64) on a bounded sample: whole
 sequences (gather + every head), in order, until about --cpu-seconds of work is done.
 
@@ -35,6 +38,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TF = 2500.0   # MI355X dense bf16 MFMA
 ROW_BYTES = 1152
 ROW_ELEMS = 576
+FP6_ROW_BYTES = 436          # ~6-bit cache: 432 bytes of codes + a 4-byte scale per row
 D_MODEL = 5120
 D_C, D_R, D_NOPE, D_V = 512, 64, 128, 128
 
@@ -139,6 +143,53 @@ def producer_timing(lib, synth, wl, dev, cache, bt, lens, steps: int):
             "bytes": nbytes, "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
             "weights": "48 rotated copies, cold", "timing": "graph replay"}
+
+
+def fp6_timing(lib, synth, wl, dev, q_abs, bt, att, o_lat, lse, ws, steps: int, splits: int,
+               bf16_ms: float):
+    """The decode over the ~6-bit cache (mla_decode_fp6) on the same workload and query: the
+    synthetic cache quantized on the GPU (mla_cache_quantize_fp6) into enough independent copies that
+    together they exceed the Infinity Cache, then `steps` calls rotating through them, each between
+    HIP events on the launch stream.  Algorithmic bytes = attended tokens x 436 (codes and scale of
+    each row); at 2,176 x heads flop per token that is past the bf16 ridge, so the matrix cores
+    (bf16 after the exact conversion) are the roofline reported."""
+    import torch
+    if wl.heads not in (64, 128) or wl.layers > 1:
+        return None
+    N = wl.tokens
+    copies = max(2, min(8, -(-400_000_000 // (N * FP6_ROW_BYTES))))
+    caches = []
+    for i in range(copies):
+        src = synth.cache_pages(wl, 100 + i, device=dev, chunk_pages=2048).view(torch.bfloat16)
+        c6 = torch.empty((wl.num_pages, lib.FP6_PAGE_BYTES), dtype=torch.uint8, device=dev)
+        lib.mla_cache_quantize_fp6(src, c6)
+        del src
+        caches.append(c6)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for i in range(3):
+        lib.mla_decode_fp6(q_abs, caches[i % copies], bt, att, wl.scale, o_lat, lse, ws, splits)
+    ev = []
+    for i in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        lib.mla_decode_fp6(q_abs, caches[i % copies], bt, att, wl.scale, o_lat, lse, ws, splits)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    del caches
+    torch.cuda.empty_cache()
+    flops = N * 2 * wl.heads * (D_C + D_R + D_C)
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = N * FP6_ROW_BYTES / (ms * 1e-3) / 1e9
+    return {"call": "mla_decode_fp6 (decode + merge kernels)",
+            "cache": "FP6 E2M3 codes + power-of-two row scale, 436 B per token",
+            "cache_copies": copies, "ms_per_call": round(ms, 5), "tokens_per_s": round(N / (ms * 1e-3), 1),
+            "bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TF, 4), "hbm_gbs": round(gbs, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bf16_cache_ms_per_call": round(bf16_ms, 5),
+            "speedup_vs_bf16_cache": round(bf16_ms / ms, 3)}
 
 
 def cpu_baseline(wl, seconds: float):
@@ -368,6 +419,9 @@ def main():
     }
     if wl.append:  # the table has a slot at each sequence's next position only when the workload appends
         line["producer"] = producer_timing(lib, synth, wl, dev, inst[0]["cache"], bt, lens, args.steps)
+    fp6 = fp6_timing(lib, synth, wl, dev, q_abs, bt, att, o_lat, lse, ws, args.steps, args.splits, dec_ms)
+    if fp6 is not None:
+        line["fp6"] = fp6
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -36,9 +36,9 @@
 // ~6-bit cache (FP6 template argument).  Pages hold 6-bit E2M3 codes with one power-of-two scale
 // per row, so every stored number is exactly a bf16 number.  Each wave copies its own rows of a
 // tile (32 / waves rows: codes and scales, 13.6 KB per tile in all) into a wave-private 3-stage
-// LDS ring, three tiles ahead, and converts them with v_cvt_scalef32_pk32_bf16_fp6 (32 codes per
-// instruction, the scale's exponent applied exactly) into the same swizzled bf16 tile layout, two
-// tiles ahead, spread over the output product.  The bf16 ring then has three stages (the tile whose
+// LDS ring, four tiles ahead (a stage is free once its tile is converted), and converts them with
+// v_cvt_scalef32_pk32_bf16_fp6 (32 codes per instruction, the scale's exponent applied exactly)
+// into the same swizzled bf16 tile layout, two tiles ahead, spread over the output product.  The bf16 ring then has three stages (the tile whose
 // output product runs, the tile whose scores run, the tile being converted) and everything after it
 // is the bf16 path unchanged.  Reading only the codes, the conversion needs no barrier of its own:
 // a wave converts exactly the rows it copied, and the barrier that opens each iteration publishes
@@ -377,6 +377,9 @@ struct Fp6Geom {
   // converted and stored two steps later, one unit in flight at a time.
   static constexpr int kRoundStep = 28 / kRounds > 8 ? 8 : 28 / kRounds;   // 8 / 5 / 3
   static_assert(kRoundStep >= 3 && 4 + kRoundStep * (kRounds - 1) + 2 < 32, "rounds fit the product");
+  // Copies inside the 36 score steps: copy j at step 2 + kCopyStep j.
+  static constexpr int kCopyStep = 32 / kCopies;                                    // 6 / 4 / 2
+  static_assert(2 + kCopyStep * (kCopies - 1) < 36, "copies fit the score product");
 };
 constexpr int kFp6Stages = 3;
 
@@ -388,25 +391,26 @@ __device__ __forceinline__ void dma4(const char* gbase, unsigned voff, unsigned 
                : "memory", "m0");
 }
 
-// This wave's copies of one tile (tile rows start at page slot slot0, nt valid rows) into its
-// region `lds` of an fp6 stage.  A ragged tile repeats its last valid row for the missing ones, so
-// every converted number is finite.  Always kCopies instructions, each with some lane active.
+// Copy j (< kCopies) of this wave's part of one tile (tile rows start at page slot slot0, nt valid
+// rows) into its region `lds` of an fp6 stage: copies 0 .. kDataCopies - 1 move 1 KB of codes each
+// (the last one partly), the final copy the scales.  A ragged tile repeats its last valid row for
+// the missing ones, so every converted number is finite.  Some lane is active in every copy, so
+// each is one instruction for the counted waits.  j must fold to a constant.
 template <int NW>
-__device__ __forceinline__ void issue_tile6(const char* page_base, int slot0, int nt, unsigned lds, int wave) {
+__device__ __forceinline__ void issue_copy6(const char* page_base, int slot0, int nt, unsigned lds, int wave, int j) {
   using G = Fp6Geom<NW>;
   const int ln = lane_id();
   const int r0 = wave * G::kRows;
-#pragma unroll
-  for (int j = 0; j < G::kDataCopies; ++j) {
+  if (j < G::kDataCopies) {
     const int o = 1024 * j + 16 * ln;
     if (j < G::kDataCopies - 1 || o < G::kDataBytes) {
       const int r = o / kFp6RowBytes;
       const int rr = min(r0 + r, nt - 1);
       dma16(page_base, (unsigned)((slot0 + rr) * kFp6RowBytes + (o - r * kFp6RowBytes)), lds + 1024 * j);
     }
-  }
-  if (ln < G::kRows)
+  } else if (ln < G::kRows) {
     dma4(page_base, (unsigned)(kPage * kFp6RowBytes + 4 * (slot0 + min(r0 + ln, nt - 1))), lds + G::kDataBytes);
+  }
 }
 
 // One conversion unit in flight: 32 codes and the row scale.
@@ -415,14 +419,17 @@ struct Fp6Unit {
   float scale;
 };
 
-// Loads unit u of this wave's rows from its fp6 region (unit u: row u / 18, codes 32 (u % 18) ..).
-// Units are numbered lane + 64 k for round k, the lane taken from lane_id() so that the address
-// arithmetic stays where it is used instead of holding registers across the tile loop.
+// Loads unit u of this wave's rows from its fp6 region (unit u: row u % R, codes 32 (u / R) ..,
+// R = rows per wave).  Rows vary fastest across lanes: 16 lanes then write 8 or 16 different rows,
+// which the tile swizzle spreads over the bank groups (two lanes per group with 8 rows, one with
+// 16), where 16 units of one row would land on two groups.  Units are numbered lane + 64 k for
+// round k, the lane taken from lane_id() so that the address arithmetic stays where it is used
+// instead of holding registers across the tile loop.
 template <int NW>
 __device__ __forceinline__ Fp6Unit fp6_load(unsigned region, int k) {
   using G = Fp6Geom<NW>;
   const int u = lane_id() + 64 * k;
-  const int r = u / (kRow / 32), g = u - r * (kRow / 32);
+  const int r = u % G::kRows, g = u / G::kRows;
   const LDS_AS char* src = (const LDS_AS char*)(uintptr_t)region + r * kFp6RowBytes + 24 * g;
   const u32x2 a = *reinterpret_cast<const LDS_AS u32x2*>(src);
   const u32x2 b = *reinterpret_cast<const LDS_AS u32x2*>(src + 8);
@@ -445,7 +452,7 @@ __device__ __forceinline__ void fp6_store(const Fp6Unit& x, int k, unsigned stag
   u32x16 v;
   asm("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2" : "=&v"(v) : "v"(x.codes), "v"(x.scale));
   const int u = lane_id() + 64 * k;
-  const int r = u / (kRow / 32), g = u - r * (kRow / 32);
+  const int r = u % G::kRows, g = u / G::kRows;
   const unsigned a0 = stage + (unsigned)tile_offset(wave * G::kRows + r, 4 * g);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -525,7 +532,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   };
   auto issue6 = [&](int page) __attribute__((always_inline)) {
     const char* pb = reinterpret_cast<const char*>(p.cache) + (size_t)page * kFp6PageBytes;
-    issue_tile6<NW>(pb, (int)((unsigned)ld.t % kPage), min(kTileTok, ld.t_end - ld.t), region6(issued), wave);
+    const int slot0 = (int)((unsigned)ld.t % kPage), nt = min(kTileTok, ld.t_end - ld.t);
+    const unsigned lds = region6(issued);
+#pragma unroll
+    for (int j = 0; j < G6::kCopies; ++j) issue_copy6<NW>(pb, slot0, nt, lds, wave, j);
     ld.advance();
     ++issued;
   };
@@ -534,15 +544,18 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     for (int s = 0; s < kFp6Stages; ++s) {
       if (ld.valid) issue6(ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage));
     }
-    // Tiles 0 and 1 are converted here, the rest two tiles ahead inside the loop.  Loads complete in
-    // issue order, so the query has landed once tile 0 has.
+    // Tiles 0 and 1 are converted here, the rest two tiles ahead inside the loop.  Once tile 0 is
+    // converted its stage takes tile 3, so the copies run four tiles ahead of the tile whose output
+    // product runs.  Loads complete in issue order, so the query has landed once tile 0 has.
     constexpr int C = G6::kCopies;
     if (issued >= 3) wait_vmcnt<2 * C>();
     else if (issued == 2) wait_vmcnt<C>();
     else wait_vmcnt<0>();
     fp6_convert_all<NW>(region6(0), (unsigned)(uintptr_t)(LDS_AS char*)ring[0], wave);
+    if (ld.valid) issue6(ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage));
     if (issued >= 2) {
-      if (issued >= 3) wait_vmcnt<C>();
+      if (issued >= 4) wait_vmcnt<2 * C>();
+      else if (issued == 3) wait_vmcnt<C>();
       else wait_vmcnt<0>();
       fp6_convert_all<NW>(region6(1), (unsigned)(uintptr_t)(LDS_AS char*)ring[1], wave);
     }
@@ -660,14 +673,23 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       bool sp_have = false;
       if constexpr (FP6) {
         // The converted tile it + 1 is published by the barrier; the block-table read for the
-        // copies of tile it + 3 is issued after this wave's own LDS writes are done, so that it
-        // overlaps the barrier instead of being waited for before it.
+        // copies of tile it + 4 (into the stage of tile it + 1, converted last iteration) is issued
+        // after this wave's own LDS writes are done, so that it overlaps the barrier instead of
+        // being waited for before it.
         wait_lgkmcnt0();
         __builtin_amdgcn_sched_barrier(0);
         sp_have = ld.valid;
-        if (ld.valid) sp_page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage);
+        if (ld.valid) {
+          sp_page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage);
+          sp_tok = (int)((unsigned)ld.t % kPage);
+          sp_lane = (unsigned)min(kTileTok, ld.t_end - ld.t);   // valid rows of the tile
+          sp_lds = region6(issued);
+          ld.advance();
+          ++issued;
+        }
         __builtin_amdgcn_s_barrier();
-        if (sp_have) issue6(sp_page);
+        asm volatile("" : "+s"(sp_page));  // the page is first needed behind the barrier
+        if (sp_have) sp_base += (size_t)sp_page * kFp6PageBytes;
       } else if constexpr (NW == 4) {
         const int ln = lane_id();
         const int tl = (ln >> 3) ^ (wave & 1);
@@ -699,6 +721,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       }
       auto spread_copy = [&](int j) __attribute__((always_inline)) {
         if constexpr (NW == 4 && !FP6) dma16_group(sp_base, sp_lane, sp_lds, j);
+      };
+      // ~6-bit cache: copy j of tile it + 4 (spread over the score product like the bf16 copies)
+      auto copy6 = [&](int j) __attribute__((always_inline)) {
+        if constexpr (FP6) {
+          if (sp_have) issue_copy6<NW>(sp_base, sp_tok, (int)sp_lane, sp_lds, wave, j);
+        }
       };
 
       // ---- softmax of tile it (base 2), lane = head, registers = tokens, spread over the next
@@ -752,6 +780,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
           if (ks == 0) mfma_v_first_nw(s_nxt, ka[0], q[0]); else mfma_v_nw(s_nxt, ka[ks % (kKAhead + 1)], q[ks]);
           softmax_step(ks);
           if ((ks & 3) == 0) spread_copy(ks >> 2);
+          if constexpr (FP6) {
+            if (ks >= 2 && (ks - 2) % G6::kCopyStep == 0 && (ks - 2) / G6::kCopyStep < G6::kCopies)
+              copy6((ks - 2) / G6::kCopyStep);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         mfma_v_drain(s_nxt);
@@ -760,6 +792,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         for (int k = 0; k < 12; ++k) softmax_step(k);
 #pragma unroll
         for (int j = 0; j < kCG; ++j) spread_copy(j);
+#pragma unroll
+        for (int j = 0; j < G6::kCopies; ++j) copy6(j);
       }
 
       if (__builtin_expect(rescale, 0)) {
@@ -823,8 +857,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
           if (i == 8) l_sum += ls0 + ls1;
           if constexpr (FP6) {
             if (conv) {
-              if (i == 4) {  // this wave's copies of tile it + 2 have landed (tile it + 3's may not)
-                if (it + 3 < issued) wait_vmcnt<G6::kCopies>();
+              if (i == 4) {  // this wave's copies of tile it + 2 have landed (those of it + 3, it + 4 may not)
+                if (it + 4 < issued) wait_vmcnt<2 * G6::kCopies>();
+                else if (it + 3 < issued) wait_vmcnt<G6::kCopies>();
                 else wait_vmcnt<0>();
               }
 #pragma unroll
