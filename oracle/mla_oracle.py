@@ -274,6 +274,34 @@ def latent_rows_batch(h, w_dkv, w_kr, positions, base: float) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------------------
+# The output projection to the hidden width (explainer Step 6: the heads' outputs are concatenated
+# and mixed by W^O, and W^UV can be folded into it)
+# --------------------------------------------------------------------------------------------------
+
+
+def hidden_out(out_heads, w_o) -> np.ndarray:
+    """out_heads [B][H][d_v] concatenated per sequence (head-major) times W^O [H * d_v][d_model]:
+    the attention block's output in the hidden width.  Reading: W^O is stored input-major, as the
+    other weights here, so the product is out @ W^O."""
+    o = _f64(out_heads)
+    B = o.shape[0]
+    return o.reshape(B, -1) @ _f64(w_o)
+
+
+def hidden_out_folded(o_lat, w_uv, w_o) -> np.ndarray:
+    """The same output with W^UV folded into W^O first (Step 6): per head the 512 x d_model matrix
+    W^UV[h] W^O[h], applied to the latent-form output o_lat [B][H][512]."""
+    o_lat, w_uv, w_o = _f64(o_lat), _f64(w_uv), _f64(w_o)
+    B, H, _ = o_lat.shape
+    d_v = w_uv.shape[2]
+    out = np.zeros((B, w_o.shape[1]))
+    for h in range(H):
+        folded = w_uv[h] @ w_o[h * d_v:(h + 1) * d_v]        # [512][d_model]
+        out += o_lat[:, h] @ folded
+    return out
+
+
+# --------------------------------------------------------------------------------------------------
 # A ~6-bit cache (explainer, the audit after Step 8: deployed V2 stores each cached number in about
 # six bits, near 26 KB per token over its 60 layers).  The pages give no format; the reading here:
 # each number is an FP6 E2M3 code (1 sign, 2 exponent, 3 mantissa bits, exponent bias 1, no

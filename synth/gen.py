@@ -40,6 +40,7 @@ Q_DIM = D_NOPE + D_R
 # stream ids (one independent counter stream per kind of input)
 S_CACHE, S_Q, S_QABS, S_WUK, S_WUV, S_NEWROW, S_GARBAGE = 1, 2, 3, 4, 5, 6, 7
 S_HIDDEN, S_WDKV, S_WKR = 8, 9, 10
+S_WO = 11
 
 _U64 = (1 << 64) - 1
 _GAMMA = 0x9E3779B97F4A7C15
@@ -297,6 +298,13 @@ def producer_weights(wl: Workload, layer: int = 0, device="cpu"):
     w_dkv = normal_bf16(stream_key(wl.seed, S_WDKV, layer), _idx(D_MODEL * D_C, device), std).view(D_MODEL, D_C)
     w_kr = normal_bf16(stream_key(wl.seed, S_WKR, layer), _idx(D_MODEL * D_R, device), std).view(D_MODEL, D_R)
     return w_dkv, w_kr
+
+
+def output_weights(wl: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
+    """W^O int16 [H * 128][5120], std 1/sqrt(H * 128): mixes the heads' outputs into the hidden
+    width."""
+    k = wl.heads * D_V
+    return normal_bf16(stream_key(wl.seed, S_WO, layer), _idx(k * D_MODEL, device), 1.0 / math.sqrt(k)).view(k, D_MODEL)
 
 
 def as_bf16(t: torch.Tensor) -> torch.Tensor:

@@ -264,3 +264,38 @@ def test_append_hidden_matches_oracle(lib, f32):
     lib.mla_cache_append_hidden(cache, bt, pos, h, wd, wk, 10000.0, ws)
     torch.cuda.synchronize()
     assert torch.equal(cache.view(torch.int16), after)
+
+
+@pytest.mark.parametrize("batch", [32, 33, 100])
+def test_append_hidden_batch_blocks(lib, batch):
+    """The producer side at the benchmark's batch (32: one full 32-row block) and past it (33 and 100:
+    two-block passes with a ragged last block), positions anywhere in their pages: every written row
+    against the oracle, every other byte unchanged."""
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(0, 3000, batch).tolist()
+    wl = synth.make_custom(lens, heads=16, seed=92 + batch, append=True)
+    say("append hidden, batch", batch)
+    dev = "cuda"
+    cache = synth.cache_pages(wl, 0, device=dev, chunk_pages=2048).view(torch.bfloat16)
+    bt = torch.as_tensor(wl.block_table, device=dev)
+    pos = torch.as_tensor(wl.lens, device=dev)
+    h_bits = synth.hidden_states(wl, 0, device=dev)
+    wd_bits, wk_bits = synth.producer_weights(wl, 0, device=dev)
+    ws = torch.empty(lib.mla_cache_append_hidden_workspace_size(batch), dtype=torch.uint8, device=dev)
+    before = cache.view(torch.int16).clone()
+    lib.mla_cache_append_hidden(cache, bt, pos, act(h_bits, False), act(wd_bits, False), act(wk_bits, False),
+                                10000.0, ws)
+    torch.cuda.synchronize()
+    after = cache.view(torch.int16).clone()
+    pages = [int(wl.block_table[b][lens[b] // 64]) for b in range(batch)]
+    slots = [lens[b] % 64 for b in range(batch)]
+    keep = torch.ones(cache.shape[:2], dtype=torch.bool, device=dev)
+    keep[pages, slots] = False
+    assert torch.equal(after[keep], before[keep])
+    got = O.bf16_to_f64(after[pages, slots].cpu().numpy())
+    ref = O.latent_rows_batch(synth.to_numpy_u16(h_bits), synth.to_numpy_u16(wd_bits),
+                              synth.to_numpy_u16(wk_bits), wl.lens, 10000.0)
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max(axis=1, keepdims=True)
+    say(f"  max err / bound {float((err / bound).max()):.3f}")
+    assert (err <= bound).all()

@@ -528,3 +528,34 @@ def test_fp6_many_rows_match_one_row():
             codes, e = O.quantize_row_fp6(bits[p, t])
             assert np.array_equal(O.unpack_fp6(pages6[p, t * 432:(t + 1) * 432]), codes)
             assert pages6[p, 27648 + 4 * t:27648 + 4 * t + 4].view(np.float32)[0] == 2.0 ** e
+
+
+# --------------------------------------------------------------------------------------------------
+# Output projection to the hidden width (explainer Step 6)
+# --------------------------------------------------------------------------------------------------
+
+def test_hidden_out_vs_brute_force():
+    """Explicit loops on a tiny non-square shape: B 2, H 3, d_v 2, d_model 5 (a transposed W^O or a
+    wrong head order fails)."""
+    rng = np.random.default_rng(21)
+    out = rng.normal(size=(2, 3, 2))
+    w_o = rng.normal(size=(6, 5))
+    want = np.zeros((2, 5))
+    for b in range(2):
+        for n in range(5):
+            for h in range(3):
+                for v in range(2):
+                    want[b, n] += out[b, h, v] * w_o[h * 2 + v, n]
+    np.testing.assert_allclose(O.hidden_out(out, w_o), want, rtol=1e-13, atol=1e-13)
+
+
+def test_hidden_out_folded_equals_two_step():
+    """The fold the explainer states (Step 6): W^UV applied after the weighted sum and then W^O
+    equals the folded per-head matrix W^UV[h] W^O[h] applied to the latent-form output."""
+    rng = np.random.default_rng(22)
+    B, H, d_c, d_v, d = 3, 4, 16, 8, 12
+    o_lat = rng.normal(size=(B, H, d_c))
+    w_uv = rng.normal(size=(H, d_c, d_v))
+    w_o = rng.normal(size=(H * d_v, d))
+    two_step = O.hidden_out(O.out_proj_batch(o_lat, w_uv), w_o)
+    np.testing.assert_allclose(O.hidden_out_folded(o_lat, w_uv, w_o), two_step, rtol=1e-12, atol=1e-12)
