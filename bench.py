@@ -11,6 +11,7 @@ Prints one JSON line.  `value` is latent-cache GB/s over the whole step (tokens 
 time), from K steps timed between two synchronisations with nothing else on the stream.
 `roofline` reports the dominant call, mla_decode, timed with HIP events on the launch stream in a
 second pass of the same K steps.
+`out_proj_hidden` times the projection of the step's per-head output to the hidden width through W^O.
 `producer` (workloads that append) times mla_cache_append_hidden, the producer side of the cache,
 graph-replayed over 48 weight copies.  `fp6` times mla_decode_fp6 over the ~6-bit form of the same
 cache (FP6 codes and a power-of-two scale per row, 436 bytes per token).
@@ -190,6 +191,39 @@ def fp6_timing(lib, synth, wl, dev, q_abs, bt, att, o_lat, lse, ws, steps: int, 
             "frac": round(tf / MFMA_BF16_PEAK_TF, 4), "hbm_gbs": round(gbs, 2),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bf16_cache_ms_per_call": round(bf16_ms, 5),
             "speedup_vs_bf16_cache": round(bf16_ms / ms, 3)}
+
+
+def out_hidden_timing(lib, synth, wl, dev, out, steps: int):
+    """The output projection to the hidden width (mla_out_proj_hidden) on the step's per-head output:
+    W^O [heads * 128][5120] rotated through enough copies to exceed the Infinity Cache, calls
+    between HIP events.  bytes = weights + per-head rows read + hidden rows written."""
+    import torch
+    if wl.layers > 1:
+        return None
+    B, H = wl.batch, wl.heads
+    wbytes = H * D_V * D_MODEL * 2
+    copies = max(2, -(-400_000_000 // wbytes))
+    ws_ = [synth.output_weights(wl, i, device=dev).view(torch.bfloat16) for i in range(copies)]
+    hidden = torch.empty(B, D_MODEL, dtype=torch.bfloat16, device=dev)
+    work = torch.empty(lib.mla_out_proj_hidden_workspace_size(B, H), dtype=torch.uint8, device=dev)
+    for i in range(3):
+        lib.mla_out_proj_hidden(out, ws_[i % copies], hidden, work)
+    torch.cuda.synchronize()
+    n = max(steps, 2 * copies)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        lib.mla_out_proj_hidden(out, ws_[i % copies], hidden, work)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    del ws_
+    torch.cuda.empty_cache()
+    nbytes = wbytes + B * H * D_V * 2 + B * D_MODEL * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"call": "mla_out_proj_hidden", "weights_bytes": wbytes, "weight_copies": copies,
+            "ms_per_call": round(ms, 5), "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(wl, seconds: float):
@@ -419,6 +453,9 @@ def main():
     }
     if wl.append:  # the table has a slot at each sequence's next position only when the workload appends
         line["producer"] = producer_timing(lib, synth, wl, dev, inst[0]["cache"], bt, lens, args.steps)
+    oh = out_hidden_timing(lib, synth, wl, dev, out, args.steps)
+    if oh is not None:
+        line["out_proj_hidden"] = oh
     fp6 = fp6_timing(lib, synth, wl, dev, q_abs, bt, att, o_lat, lse, ws, args.steps, args.splits, dec_ms)
     if fp6 is not None:
         line["fp6"] = fp6

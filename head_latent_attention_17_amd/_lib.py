@@ -20,7 +20,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTY
           -7: "MLA_ERR_HIP"}
 EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", "mla_cache_append",
            "mla_absorb_q", "mla_decode", "mla_out_proj", "mla_cache_append_hidden_workspace_size",
-           "mla_cache_append_hidden", "mla_cache_append_fp6", "mla_cache_quantize_fp6", "mla_decode_fp6")
+           "mla_cache_append_hidden", "mla_cache_append_fp6", "mla_cache_quantize_fp6", "mla_decode_fp6",
+           "mla_out_proj_hidden_workspace_size", "mla_out_proj_hidden")
 FP6_PAGE_BYTES = 27904   # MLA_FP6_PAGE_BYTES: 64 rows of 432 code bytes, then 64 float32 scales
 
 if not os.path.exists(LIB_PATH):
@@ -53,6 +54,10 @@ lib.mla_cache_quantize_fp6.restype = _i
 lib.mla_cache_quantize_fp6.argtypes = [_p, _p, _i, _i, _p]
 lib.mla_decode_fp6.restype = _i
 lib.mla_decode_fp6.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _p, _sz, _i, _i, _p]
+lib.mla_out_proj_hidden_workspace_size.restype = _sz
+lib.mla_out_proj_hidden_workspace_size.argtypes = [_i, _i, _i]
+lib.mla_out_proj_hidden.restype = _i
+lib.mla_out_proj_hidden.argtypes = [_p, _p, _p, _i, _i, _p, _sz, _i, _p]
 
 
 class MLAError(RuntimeError):
@@ -193,3 +198,16 @@ def mla_out_proj(o_lat, w_uv, out, stream=None):
     _dev(o_lat, w_uv, out)
     _check(lib.mla_out_proj(_ptr(o_lat), _ptr(w_uv), _ptr(out), o_lat.shape[0], o_lat.shape[1],
                             _dtype_of(o_lat), _stream(stream)), "mla_out_proj")
+
+
+def mla_out_proj_hidden_workspace_size(batch: int, num_heads: int, dtype: int = MLA_BF16) -> int:
+    return int(lib.mla_out_proj_hidden_workspace_size(batch, num_heads, dtype))
+
+
+def mla_out_proj_hidden(out, w_o, hidden, workspace=None, stream=None):
+    """out [B][H][128] -> hidden [B][5120] = out flattened head-major @ w_o [H * 128][5120]."""
+    _dev(out, w_o, hidden, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.mla_out_proj_hidden(_ptr(out), _ptr(w_o), _ptr(hidden), out.shape[0], out.shape[1],
+                                   _ptr(workspace), ws_bytes, _dtype_of(out), _stream(stream)),
+           "mla_out_proj_hidden")

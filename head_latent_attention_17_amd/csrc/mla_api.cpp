@@ -58,7 +58,7 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_abi_version(void) { return 102; }
+int mla_abi_version(void) { return 103; }
 
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype) {
@@ -233,6 +233,27 @@ mla_status mla_cache_quantize_fp6(const void* kv_cache, void* kv_cache6, int num
   if (num_pages == 0) return MLA_OK;
   if (!kv_cache || !kv_cache6) return MLA_ERR_NULL;
   hipError_t e = launch_quantize_pages_fp6(kv_cache, kv_cache6, num_pages, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_out_proj_hidden_workspace_size(int batch, int num_heads, mla_dtype dtype) {
+  if (batch < 0 || !valid_heads(num_heads) || !valid_dtype(dtype)) return 0;
+  return dtype == MLA_F32 ? 0 : out_proj_hidden_workspace_bytes(batch, num_heads);
+}
+
+mla_status mla_out_proj_hidden(const void* out, const void* w_o, void* hidden, int batch, int num_heads,
+                               void* workspace, size_t workspace_bytes_given, mla_dtype dtype,
+                               hipStream_t stream) {
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (batch < 0) return MLA_ERR_SHAPE;
+  if (!valid_heads(num_heads)) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!out || !w_o || !hidden) return MLA_ERR_NULL;
+  const bool f32 = dtype == MLA_F32;
+  if (!f32 && (!workspace || workspace_bytes_given < out_proj_hidden_workspace_bytes(batch, num_heads)))
+    return MLA_ERR_WORKSPACE;
+  hipError_t e = launch_out_proj_hidden(out, w_o, hidden, batch, num_heads, static_cast<float*>(workspace), f32,
+                                        stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

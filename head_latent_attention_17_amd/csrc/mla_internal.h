@@ -67,6 +67,11 @@ hipError_t launch_append_fp6(void* cache, const int32_t* block_table, int max_bl
                              const int32_t* positions, const void* c_new, const void* kpe_new, int batch,
                              bool f32, hipStream_t s);
 hipError_t launch_quantize_pages_fp6(const void* src, void* dst, int num_pages, hipStream_t s);
+// Output projection to the hidden width: hidden [B][5120] = out [B][heads * 128] @ W^O; part is the
+// fp32 workspace of out_proj_hidden_workspace_bytes(batch, heads) (heads >= 16).
+hipError_t launch_out_proj_hidden(const void* out, const void* w_o, void* hidden, int batch, int heads,
+                                  float* part, bool f32, hipStream_t s);
+size_t out_proj_hidden_workspace_bytes(int batch, int heads);
 
 // Device-side check of block-table entries and lengths (append = false) or append positions
 // (append = true); synchronises s.  *bad is set when an entry is out of range.

@@ -203,6 +203,22 @@ mla_status mla_decode_fp6(const void* q_abs, const void* kv_cache6, int num_page
 mla_status mla_out_proj(const void* o_lat, const void* w_uv, void* out, int batch, int num_heads,
                         mla_dtype dtype, hipStream_t stream);
 
+/*
+ * The attention block's output in the hidden width (explainer Step 6: the heads' outputs are
+ * concatenated and mixed by W^O, with W^UV applied before it):
+ *   hidden[b][:] = out[b] flattened head-major (num_heads * 128) @ W^O      (5120 wide)
+ *   out     [batch][num_heads][128] (mla_out_proj's output), w_o [num_heads * 128][5120] input-major,
+ *   hidden  [batch][5120]; bf16 with fp32 accumulation (MLA_BF16) or fp32 throughout (MLA_F32).
+ * W^UV is not folded into W^O here: the folded per-head 512 x 5120 matrices would hold 3.6 times
+ * the weight bytes of W^UV and W^O together, and decode streams every weight byte per step.
+ * workspace: at least mla_out_proj_hidden_workspace_size(batch, num_heads, dtype) bytes (fp32
+ * partial sums; none are needed for MLA_F32), contents irrelevant, used only during the call.
+ * Errors as mla_out_proj, plus MLA_ERR_WORKSPACE.
+ */
+size_t mla_out_proj_hidden_workspace_size(int batch, int num_heads, mla_dtype dtype);
+mla_status mla_out_proj_hidden(const void* out, const void* w_o, void* hidden, int batch, int num_heads,
+                               void* workspace, size_t workspace_bytes, mla_dtype dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

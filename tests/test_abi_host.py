@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.mla_abi_version() == 102
+    assert L.mla_abi_version() == 103
     for code, name in L.STATUS.items():
         assert L.mla_status_string(code).startswith(name)
     assert "unknown" in L.mla_status_string(12345)
@@ -179,3 +179,23 @@ def test_fp6_cache_validation():
     assert a(FAKE, 0, 64, FAKE, 1, FAKE, FAKE, FAKE, 2, 0, None) == -2
     assert a(FAKE, 8, 64, FAKE, 1, FAKE, FAKE, FAKE, 2, 5, None) == -3
     assert a(None, 0, 64, None, 1, None, None, None, 0, 0, None) == 0
+
+
+def test_out_proj_hidden_validation_and_workspace():
+    """Output projection to the hidden width: workspace = (heads * 128 / 1024) fp32 partial rows of
+    5,120 per sequence in bf16 mode, none in fp32 mode; host-side validation before any launch."""
+    L = _lib()
+    assert L.mla_out_proj_hidden_workspace_size(32, 128) == 16 * 32 * 5120 * 4
+    assert L.mla_out_proj_hidden_workspace_size(3, 16) == 2 * 3 * 5120 * 4
+    assert L.mla_out_proj_hidden_workspace_size(3, 16, 1) == 0
+    assert L.mla_out_proj_hidden_workspace_size(3, 100) == 0
+    assert L.mla_out_proj_hidden_workspace_size(-1, 128) == 0
+    f = L.lib.mla_out_proj_hidden
+    ws = 16 * 2 * 5120 * 4
+    assert f(FAKE, FAKE, FAKE, 2, 128, FAKE, ws, 9, None) == -3
+    assert f(FAKE, FAKE, FAKE, -1, 128, FAKE, ws, 0, None) == -2
+    assert f(FAKE, FAKE, FAKE, 2, 96, FAKE, ws, 0, None) == -5
+    assert f(None, FAKE, FAKE, 2, 128, FAKE, ws, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, 2, 128, None, ws, 0, None) == -4
+    assert f(FAKE, FAKE, FAKE, 2, 128, FAKE, ws - 1, 0, None) == -4
+    assert f(None, None, None, 0, 128, None, 0, 0, None) == 0

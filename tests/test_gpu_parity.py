@@ -299,3 +299,33 @@ def test_append_hidden_batch_blocks(lib, batch):
     bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max(axis=1, keepdims=True)
     say(f"  max err / bound {float((err / bound).max()):.3f}")
     assert (err <= bound).all()
+
+
+@pytest.mark.parametrize("heads,batch,f32", [(16, 3, False), (128, 32, False), (64, 65, False),
+                                             (128, 100, False), (16, 5, True)])
+def test_out_proj_hidden_matches_oracle(lib, heads, batch, f32):
+    """Output projection to the hidden width (explainer Step 6): out flattened head-major times W^O,
+    one batch block, two blocks with a ragged tail, and two groups of 64 rows; bf16 within one
+    rounding of the oracle plus fp32 accumulation, fp32 mode within 1e-4."""
+    wl = synth.make_custom([5] * batch, heads=heads, seed=120 + heads + batch)
+    say("out_proj_hidden", heads, batch, "f32" if f32 else "bf16")
+    dev = "cuda"
+    o_bits = synth.queries(wl, 0, device=dev)[..., :synth.D_V].contiguous()   # any seeded input of this shape
+    w_bits = synth.output_weights(wl, 0, device=dev)
+    o_in, w_in = act(o_bits, f32), act(w_bits, f32)
+    hidden = torch.empty(batch, synth.D_MODEL, dtype=torch.float32 if f32 else torch.bfloat16, device=dev)
+    n = lib.mla_out_proj_hidden_workspace_size(batch, heads, lib.MLA_F32 if f32 else lib.MLA_BF16)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    lib.mla_out_proj_hidden(o_in, w_in, hidden, ws)
+    torch.cuda.synchronize()
+    got = to_host_f64(hidden)
+    ref = O.hidden_out(synth.to_numpy_u16(o_bits), synth.to_numpy_u16(w_bits))
+    err = np.abs(got - ref)
+    if f32:
+        e = rel_err(got, ref)
+        say(f"  err {e:.3e}")
+        assert e <= F32_TOL
+    else:
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max(axis=1, keepdims=True)
+        say(f"  max err / bound {float((err / bound).max()):.3f}")
+        assert (err <= bound).all()
