@@ -302,6 +302,54 @@ def hidden_out_folded(o_lat, w_uv, w_o) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------------------
+# Attention over the top-k tokens of a cheap index (wiki "KV cache data movement minimization":
+# score every token's cheap index vector against the query, keep the k best, and run attention
+# over those rows only)
+# --------------------------------------------------------------------------------------------------
+
+INDEX_DIM = 128   # reading: 128 int8 numbers per token's index vector
+
+
+def index_scores(index_cache, block_table, b: int, length: int, q_index) -> np.ndarray:
+    """Exact integer scores q_index . i_t of sequence b's tokens t < length (int8 vectors, so the
+    scores are exact in int64)."""
+    pages, slots = page_and_slot(block_table, b, np.arange(length), index_cache.shape[1])
+    vecs = np.asarray(index_cache)[pages, slots].astype(np.int64)          # [length][128]
+    return vecs @ np.asarray(q_index).astype(np.int64)
+
+
+def top_k_positions(scores, k: int) -> np.ndarray:
+    """The k highest-scoring positions (all of them when there are at most k), ties going to the
+    earlier position; returned in increasing position order."""
+    scores = np.asarray(scores)
+    n = scores.shape[0]
+    if n <= k:
+        return np.arange(n)
+    order = sorted(range(n), key=lambda t: (-int(scores[t]), t))
+    return np.sort(np.array(order[:k]))
+
+
+def sparse_latent_decode(q_abs, cache, block_table, seq_lens, index_cache, q_index, k: int, scale,
+                         d_c=512, batch=None, heads=None):
+    """Latent decode over each sequence's top-k tokens only: (o_lat [B][H][d_c], lse [B][H],
+    positions per sequence)."""
+    q_abs = _f64(q_abs)
+    B, H, _ = q_abs.shape
+    o = np.full((B, H, d_c), np.nan)
+    lse = np.full((B, H), np.nan)
+    chosen = {}
+    for b in _sel(B, batch):
+        n = int(seq_lens[b])
+        pos = top_k_positions(index_scores(index_cache, block_table, b, n, q_index[b]), k)
+        chosen[b] = pos
+        pg, sl = page_and_slot(block_table, b, pos, cache.shape[1])
+        rows = _f64(np.asarray(cache)[pg, sl]) if len(pos) else np.zeros((0, cache.shape[2]))
+        for h in _sel(H, heads):
+            o[b, h], lse[b, h], _ = latent_attention(q_abs[b, h], rows, d_c, scale)
+    return o, lse, chosen
+
+
+# --------------------------------------------------------------------------------------------------
 # A ~6-bit cache (explainer, the audit after Step 8: deployed V2 stores each cached number in about
 # six bits, near 26 KB per token over its 60 layers).  The pages give no format; the reading here:
 # each number is an FP6 E2M3 code (1 sign, 2 exponent, 3 mantissa bits, exponent bias 1, no

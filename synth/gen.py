@@ -41,6 +41,8 @@ Q_DIM = D_NOPE + D_R
 S_CACHE, S_Q, S_QABS, S_WUK, S_WUV, S_NEWROW, S_GARBAGE = 1, 2, 3, 4, 5, 6, 7
 S_HIDDEN, S_WDKV, S_WKR = 8, 9, 10
 S_WO = 11
+S_INDEX, S_QINDEX = 12, 13
+INDEX_DIM = 128  # int8 numbers in a token's cheap index vector
 
 _U64 = (1 << 64) - 1
 _GAMMA = 0x9E3779B97F4A7C15
@@ -305,6 +307,25 @@ def output_weights(wl: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
     width."""
     k = wl.heads * D_V
     return normal_bf16(stream_key(wl.seed, S_WO, layer), _idx(k * D_MODEL, device), 1.0 / math.sqrt(k)).view(k, D_MODEL)
+
+
+def uniform_int8(key: int, index: torch.Tensor) -> torch.Tensor:
+    """Integers uniform on [-127, 127] for counters ``index`` (int8)."""
+    z = raw_u64(key, index)
+    return ((_lsr(z, 32) % 255) - 127).to(torch.int8)
+
+
+def index_cache(wl: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
+    """Each token's cheap index vector, int8 [num_pages][64][128], uniform on [-127, 127]; every slot
+    of every page is drawn (slots past a length are never scored)."""
+    n = wl.num_pages * PAGE * INDEX_DIM
+    return uniform_int8(stream_key(wl.seed, S_INDEX, layer), _idx(n, device)).view(wl.num_pages, PAGE, INDEX_DIM)
+
+
+def index_queries(wl: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
+    """Each sequence's index query, int8 [B][128], uniform on [-127, 127]."""
+    n = wl.batch * INDEX_DIM
+    return uniform_int8(stream_key(wl.seed, S_QINDEX, layer), _idx(n, device)).view(wl.batch, INDEX_DIM)
 
 
 def as_bf16(t: torch.Tensor) -> torch.Tensor:

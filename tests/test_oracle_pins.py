@@ -559,3 +559,57 @@ def test_hidden_out_folded_equals_two_step():
     w_o = rng.normal(size=(H * d_v, d))
     two_step = O.hidden_out(O.out_proj_batch(o_lat, w_uv), w_o)
     np.testing.assert_allclose(O.hidden_out_folded(o_lat, w_uv, w_o), two_step, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------------------------------
+# Top-k selection over a cheap index (wiki "KV cache data movement minimization")
+# --------------------------------------------------------------------------------------------------
+
+def test_top_k_by_hand():
+    """Hand-worked selections: largest scores win, ties go to the earlier position, the result is in
+    position order, and short sequences keep every token."""
+    assert O.top_k_positions([5, 1, 9, 3, 9, 0], 3).tolist() == [0, 2, 4]
+    assert O.top_k_positions([2, 2, 2, 2], 2).tolist() == [0, 1]
+    assert O.top_k_positions([-3, -1, -2], 1).tolist() == [1]
+    assert O.top_k_positions([7, 7], 5).tolist() == [0, 1]
+    assert O.top_k_positions([], 4).tolist() == []
+
+
+def test_top_k_against_brute_force():
+    """Brute force: a position is kept exactly when fewer than k positions beat it, where t beats u
+    if its score is higher or equal with t < u."""
+    rng = np.random.default_rng(31)
+    for _ in range(50):
+        n = int(rng.integers(1, 60))
+        k = int(rng.integers(1, 20))
+        sc = rng.integers(-4, 5, n)                      # many ties
+        keep = [t for t in range(n)
+                if sum(1 for u in range(n) if sc[u] > sc[t] or (sc[u] == sc[t] and u < t)) < k]
+        assert O.top_k_positions(sc, k).tolist() == keep
+
+
+def test_index_scores_through_the_table():
+    """Scores gathered through a shuffled table equal the dot products written out by loops."""
+    rng = np.random.default_rng(32)
+    idx = rng.integers(-128, 128, (4, 64, 128)).astype(np.int8)
+    bt = np.array([[3, 1, -1], [0, 2, -1]], np.int32)
+    q = rng.integers(-128, 128, 128).astype(np.int8)
+    got = O.index_scores(idx, bt, 0, 100, q)
+    for t in (0, 63, 64, 99):
+        page = bt[0, t // 64]
+        assert got[t] == sum(int(q[j]) * int(idx[page, t % 64, j]) for j in range(128))
+
+
+def test_sparse_decode_with_k_at_least_the_length_is_dense():
+    """With k >= every length the top-k attention is the full attention, bit for bit."""
+    rng = np.random.default_rng(33)
+    cache = rng.integers(0, 1 << 16, (3, 64, 576)).astype(np.uint16) & 0x3FFF   # finite bf16 patterns
+    idx = rng.integers(-128, 128, (3, 64, 128)).astype(np.int8)
+    bt = np.array([[2, 0], [1, -1]], np.int32)
+    lens = np.array([100, 40])
+    q = rng.normal(0, 0.3, (2, 4, 576))
+    qi = rng.integers(-128, 128, (2, 128)).astype(np.int8)
+    o, l, chosen = O.sparse_latent_decode(q, cache, bt, lens, idx, qi, 128, 0.05)
+    o2, l2 = O.latent_decode_batch(q, cache, bt, lens, 0.05)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    assert chosen[0].tolist() == list(range(100))
