@@ -11,6 +11,8 @@ Prints one JSON line.  `value` is latent-cache GB/s over the whole step (tokens 
 time), from K steps timed between two synchronisations with nothing else on the stream.
 `roofline` reports the dominant call, mla_decode, timed with HIP events on the launch stream in a
 second pass of the same K steps.
+`sparse_topk` times attention over each sequence's 2,048 best tokens of a cheap int8 index (scores and
+top-k, gather of the kept rows, decode over them) against the dense decode call.
 `out_proj_hidden` times the projection of the step's per-head output to the hidden width through W^O.
 `producer` (workloads that append) times mla_cache_append_hidden, the producer side of the cache,
 graph-replayed over 48 weight copies.  `fp6` times mla_decode_fp6 over the ~6-bit form of the same
@@ -224,6 +226,59 @@ def out_hidden_timing(lib, synth, wl, dev, out, steps: int):
     return {"call": "mla_out_proj_hidden", "weights_bytes": wbytes, "weight_copies": copies,
             "ms_per_call": round(ms, 5), "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_ms: float, k: int = 2048):
+    """Attention over the top-k tokens of a cheap int8 index on the same workload: index scores and
+    top-k (mla_index_topk), the gather of the kept rows (mla_gather_rows) and the decode over them
+    (mla_decode), each stage between HIP events, `steps` times.  Algorithmic bytes = every token's
+    128-byte index vector + each kept row once (1,152 bytes)."""
+    import torch
+    if wl.layers > 1:
+        return None
+    B, H = wl.batch, wl.heads
+    idx = synth.index_cache(wl, 0, device=dev)
+    qi = synth.index_queries(wl, 0, device=dev)
+    pos = torch.empty((B, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws_t = torch.empty(lib.mla_index_topk_workspace_size(B, wl.max_blocks), dtype=torch.uint8, device=dev)
+    pk = -(-k // 64)
+    comp = torch.empty((B * pk, 64, ROW_ELEMS), dtype=torch.bfloat16, device=dev)
+    comp_bt = torch.empty((B, pk), dtype=torch.int32, device=dev)
+    ws_d = torch.empty(lib.mla_decode_workspace_size(B, H, pk, 0), dtype=torch.uint8, device=dev)
+    o_lat = torch.empty(B, H, D_C, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run(ev=None):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if ev is not None else None
+        if marks: marks[0].record(stream)
+        lib.mla_index_topk(idx, bt, att, qi, k, pos, cnt, ws_t)
+        if marks: marks[1].record(stream)
+        lib.mla_gather_rows(cache, bt, pos, cnt, comp, comp_bt)
+        if marks: marks[2].record(stream)
+        lib.mla_decode(q_abs, comp, comp_bt, cnt, wl.scale, o_lat, lse, ws_d)
+        if marks:
+            marks[3].record(stream)
+            ev.append(marks)
+
+    for _ in range(3):
+        run()
+    ev = []
+    for _ in range(steps):
+        run(ev)
+    torch.cuda.synchronize()
+    st = [sum(m[i].elapsed_time(m[i + 1]) for m in ev) / len(ev) for i in range(3)]
+    ms = sum(st)
+    kept = int(cnt.sum().item())
+    nbytes = wl.tokens * 128 + kept * ROW_BYTES
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"calls": "mla_index_topk + mla_gather_rows + mla_decode", "k": k, "kept_tokens": kept,
+            "scored_tokens": wl.tokens, "ms_per_call": round(ms, 5),
+            "ms_topk": round(st[0], 5), "ms_gather": round(st[1], 5), "ms_decode": round(st[2], 5),
+            "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "dense_decode_ms": round(dense_ms, 5),
+            "speedup_vs_dense": round(dense_ms / ms, 3)}
 
 
 def cpu_baseline(wl, seconds: float):
@@ -453,6 +508,9 @@ def main():
     }
     if wl.append:  # the table has a slot at each sequence's next position only when the workload appends
         line["producer"] = producer_timing(lib, synth, wl, dev, inst[0]["cache"], bt, lens, args.steps)
+    sp = sparse_timing(lib, synth, wl, dev, q_abs, bt, att, inst[0]["cache"], args.steps, dec_ms)
+    if sp is not None:
+        line["sparse_topk"] = sp
     oh = out_hidden_timing(lib, synth, wl, dev, out, args.steps)
     if oh is not None:
         line["out_proj_hidden"] = oh

@@ -21,7 +21,9 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTY
 EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", "mla_cache_append",
            "mla_absorb_q", "mla_decode", "mla_out_proj", "mla_cache_append_hidden_workspace_size",
            "mla_cache_append_hidden", "mla_cache_append_fp6", "mla_cache_quantize_fp6", "mla_decode_fp6",
-           "mla_out_proj_hidden_workspace_size", "mla_out_proj_hidden")
+           "mla_out_proj_hidden_workspace_size", "mla_out_proj_hidden", "mla_index_topk_workspace_size",
+           "mla_index_topk", "mla_gather_rows")
+INDEX_DIM = 128          # MLA_INDEX_DIM: int8 numbers in a token's index vector
 FP6_PAGE_BYTES = 27904   # MLA_FP6_PAGE_BYTES: 64 rows of 432 code bytes, then 64 float32 scales
 
 if not os.path.exists(LIB_PATH):
@@ -58,6 +60,12 @@ lib.mla_out_proj_hidden_workspace_size.restype = _sz
 lib.mla_out_proj_hidden_workspace_size.argtypes = [_i, _i, _i]
 lib.mla_out_proj_hidden.restype = _i
 lib.mla_out_proj_hidden.argtypes = [_p, _p, _p, _i, _i, _p, _sz, _i, _p]
+lib.mla_index_topk_workspace_size.restype = _sz
+lib.mla_index_topk_workspace_size.argtypes = [_i, _i]
+lib.mla_index_topk.restype = _i
+lib.mla_index_topk.argtypes = [_p, _i, _i, _p, _i, _p, _p, _i, _i, _p, _p, _p, _sz, _p]
+lib.mla_gather_rows.restype = _i
+lib.mla_gather_rows.argtypes = [_p, _i, _i, _p, _i, _p, _p, _i, _i, _p, _p, _p]
 
 
 class MLAError(RuntimeError):
@@ -211,3 +219,27 @@ def mla_out_proj_hidden(out, w_o, hidden, workspace=None, stream=None):
     _check(lib.mla_out_proj_hidden(_ptr(out), _ptr(w_o), _ptr(hidden), out.shape[0], out.shape[1],
                                    _ptr(workspace), ws_bytes, _dtype_of(out), _stream(stream)),
            "mla_out_proj_hidden")
+
+
+def mla_index_topk_workspace_size(batch: int, max_blocks_per_seq: int) -> int:
+    return int(lib.mla_index_topk_workspace_size(batch, max_blocks_per_seq))
+
+
+def mla_index_topk(index_cache, block_table, seq_lens, q_index, k, positions, counts, workspace, stream=None):
+    """index_cache int8 [pages][64][128], q_index int8 [B][128] -> positions int32 [B][k] (increasing)
+    and counts int32 [B] of each sequence's k best-scoring tokens."""
+    _dev(index_cache, block_table, seq_lens, q_index, positions, counts, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.mla_index_topk(_ptr(index_cache), index_cache.shape[0], index_cache.shape[1], _ptr(block_table),
+                              block_table.shape[1], _ptr(seq_lens), _ptr(q_index), seq_lens.shape[0], int(k),
+                              _ptr(positions), _ptr(counts), _ptr(workspace), ws_bytes, _stream(stream)),
+           "mla_index_topk")
+
+
+def mla_gather_rows(kv_cache, block_table, positions, counts, out_cache, out_block_table, stream=None):
+    """Kept rows into compact pages out_cache [B * P][64][576] with out_block_table int32 [B][P]."""
+    _dev(kv_cache, block_table, positions, counts, out_cache, out_block_table)
+    _check(lib.mla_gather_rows(_ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1], _ptr(block_table),
+                               block_table.shape[1], _ptr(positions), _ptr(counts), positions.shape[0],
+                               positions.shape[1], _ptr(out_cache), _ptr(out_block_table), _stream(stream)),
+           "mla_gather_rows")

@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libmla.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["mla_api.cpp", "proj.hip", "proj_mfma.hip", "decode.hip", "decode_mfma.hip", "checks.hip",
-           "producer.hip", "lowbit.hip", "outproj.hip"]
+           "producer.hip", "lowbit.hip", "outproj.hip", "sparse.hip"]
 ARCH = "gfx950"
 
 

@@ -58,7 +58,7 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_abi_version(void) { return 103; }
+int mla_abi_version(void) { return 104; }
 
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype) {
@@ -254,6 +254,44 @@ mla_status mla_out_proj_hidden(const void* out, const void* w_o, void* hidden, i
     return MLA_ERR_WORKSPACE;
   hipError_t e = launch_out_proj_hidden(out, w_o, hidden, batch, num_heads, static_cast<float*>(workspace), f32,
                                         stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_index_topk_workspace_size(int batch, int max_blocks_per_seq) {
+  if (batch < 0 || max_blocks_per_seq < 1) return 0;
+  return index_topk_workspace_bytes(batch, max_blocks_per_seq);
+}
+
+mla_status mla_index_topk(const int8_t* index_cache, int num_pages, int page_size, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* seq_lens, const int8_t* q_index, int batch, int k,
+                          int32_t* positions, int32_t* counts, void* workspace, size_t workspace_bytes_given,
+                          hipStream_t stream) {
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1 || k < 1) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!index_cache || !block_table || !seq_lens || !q_index || !positions || !counts) return MLA_ERR_NULL;
+  if (!workspace || workspace_bytes_given < index_topk_workspace_bytes(batch, max_blocks_per_seq))
+    return MLA_ERR_WORKSPACE;
+  if (debug_checks_enabled()) {
+    bool bad = false;
+    if (check_tables(block_table, max_blocks_per_seq, seq_lens, batch, num_pages, false, stream, &bad) != hipSuccess)
+      return MLA_ERR_HIP;
+    if (bad) return MLA_ERR_BLOCK_TABLE;
+  }
+  hipError_t e = launch_index_topk(index_cache, block_table, max_blocks_per_seq, seq_lens, q_index, batch, k,
+                                   positions, counts, workspace, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_gather_rows(const void* kv_cache, int num_pages, int page_size, const int32_t* block_table,
+                           int max_blocks_per_seq, const int32_t* positions, const int32_t* counts, int batch,
+                           int k, void* out_cache, int32_t* out_block_table, hipStream_t stream) {
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1 || k < 1) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!kv_cache || !block_table || !positions || !counts || !out_cache || !out_block_table) return MLA_ERR_NULL;
+  hipError_t e = launch_gather_rows(kv_cache, block_table, max_blocks_per_seq, positions, counts, batch, k, out_cache,
+                                    out_block_table, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

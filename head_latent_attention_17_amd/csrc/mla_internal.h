@@ -72,6 +72,14 @@ hipError_t launch_quantize_pages_fp6(const void* src, void* dst, int num_pages, 
 hipError_t launch_out_proj_hidden(const void* out, const void* w_o, void* hidden, int batch, int heads,
                                   float* part, bool f32, hipStream_t s);
 size_t out_proj_hidden_workspace_bytes(int batch, int heads);
+// Top-k over a cheap int8 index and the gather of the kept rows into compact pages.
+hipError_t launch_index_topk(const int8_t* index_cache, const int32_t* block_table, int max_blocks,
+                             const int32_t* seq_lens, const int8_t* q_index, int batch, int k, int32_t* positions,
+                             int32_t* counts, void* workspace, hipStream_t s);
+hipError_t launch_gather_rows(const void* cache, const int32_t* block_table, int max_blocks,
+                              const int32_t* positions, const int32_t* counts, int batch, int k, void* out,
+                              int32_t* out_bt, hipStream_t s);
+size_t index_topk_workspace_bytes(int batch, int max_blocks);
 
 // Device-side check of block-table entries and lengths (append = false) or append positions
 // (append = true); synchronises s.  *bad is set when an entry is out of range.

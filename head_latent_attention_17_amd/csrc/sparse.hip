@@ -1,0 +1,338 @@
+// Attention over the top-k tokens of a cheap index ("DeepSeek (AI)" wiki, "KV cache data movement
+// minimization": retrieval is bandwidth-bound, so each token also carries a cheap index vector; a
+// decode query scores all of them, keeps the k best, and attention reads only those rows).
+// Reading: an index vector is 128 int8 numbers, so a score is an exact integer; ties go to the
+// earlier position; a sequence of at most k tokens keeps them all.
+//
+//   scoring   s_t = q_index[b] . i_t for t < len_b (8 lanes per token, 16 bytes and four
+//             v_dot4_i32_i8 each), written as int32, with a histogram of the high bits of the
+//             order-preserving key s_t + 2^21 (4,096 bins, counted in LDS per 1,024-token chunk).
+//   select    a two-pass radix select over many workgroups: the high bin holding the k-th largest
+//             key, then a 2,048-bin histogram of the low bits inside it, give the k-th largest key
+//             T and how many keys equal to T are kept (the earliest ones).
+//   write     per chunk, keys above T and equal to T are counted; one scan over the chunks gives
+//             each chunk its output offset; each chunk then writes its kept positions, so the
+//             result is in increasing position order.
+//   gather    copies the kept rows into compact pages (sequence b owns pages b P .. b P + P - 1,
+//             P = ceil(k / 64)) and writes their block table, so that mla_decode runs over them
+//             unchanged.
+#include "mla_device.h"
+
+namespace mla {
+namespace {
+
+constexpr int kIndexDim = 128;
+constexpr int kChunk = 1024;          // positions per workgroup in the scoring and selection passes
+constexpr int kBins1 = 4096;          // key >> 11: keys are score + 2^21, in [0, 2^22]
+constexpr int kBins2 = 2048;          // key & 2047
+
+// Workspace layout (int32), per sequence b:
+//   scores [B][stride]; hist1 [B][4096]; hist2 [B][2048]; pick [B][4] (hi bin, left after it,
+//   threshold key T, keys equal to T to keep; T = -1 keeps every token); chunk [B][nchunks][2]
+//   (keys above T, keys equal to T) turned into (output offset, equal keys before the chunk).
+struct TopkWs {
+  int32_t* scores;
+  int32_t* hist1;
+  int32_t* hist2;
+  int32_t* pick;
+  int32_t* chunk;
+  int stride, nchunks;
+};
+
+__device__ __forceinline__ int key_of(int32_t s) { return s + (1 << 21); }
+
+__global__ __launch_bounds__(256) void topk_clear_kernel(TopkWs w) {
+  const int b = blockIdx.x;
+  for (int i = threadIdx.x; i < kBins1; i += 256) w.hist1[(size_t)b * kBins1 + i] = 0;
+  for (int i = threadIdx.x; i < kBins2; i += 256) w.hist2[(size_t)b * kBins2 + i] = 0;
+}
+
+// Scores of chunk blockIdx.x of sequence b (8 lanes per token, 32 tokens per step), plus the
+// histogram of their high key bits, gathered in LDS and added to the sequence's histogram.
+__global__ __launch_bounds__(256) void index_score_kernel(const int8_t* __restrict__ index_cache,
+                                                          const int32_t* __restrict__ block_table, int max_blocks,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          const int8_t* __restrict__ q_index, TopkWs w) {
+  __shared__ int hist[kBins1];
+  const int b = blockIdx.y;
+  const int len = seq_lens[b];
+  const int t0 = blockIdx.x * kChunk;
+  if (t0 >= len) return;
+  for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int part = threadIdx.x & 7;  // 16-byte part of the vector
+  const int4 q = *reinterpret_cast<const int4*>(q_index + (size_t)b * kIndexDim + 16 * part);
+  for (int step = 0; step < kChunk / 32; ++step) {
+    const int t = t0 + step * 32 + (threadIdx.x >> 3);
+    int s = 0;
+    if (t < len) {
+      const int page = block_table[(size_t)b * max_blocks + t / kPage];
+      const int4 v = *reinterpret_cast<const int4*>(index_cache + ((size_t)page * kPage + t % kPage) * kIndexDim + 16 * part);
+      s = __builtin_amdgcn_sdot4(v.x, q.x, s, false);
+      s = __builtin_amdgcn_sdot4(v.y, q.y, s, false);
+      s = __builtin_amdgcn_sdot4(v.z, q.z, s, false);
+      s = __builtin_amdgcn_sdot4(v.w, q.w, s, false);
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 4, 64);
+    if (t < len && part == 0) {
+      w.scores[(size_t)b * w.stride + t] = s;
+      atomicAdd(&hist[key_of(s) >> 11], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins1; i += 256)
+    if (hist[i]) atomicAdd(&w.hist1[(size_t)b * kBins1 + i], hist[i]);
+}
+
+// Inclusive scan over a workgroup of NT threads (one value each) through the wave totals in LDS;
+// the workgroup total goes to *total.
+template <int NT>
+__device__ __forceinline__ int block_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int i = 0; i < NT / 64; ++i) {
+      const int x = wsum[i];
+      wsum[i] = acc;
+      acc += x;
+    }
+    *total = acc;
+  }
+  __syncthreads();
+  const int r = v + wsum[wave];
+  __syncthreads();  // wsum is reused by the next scan
+  return r;
+}
+
+// Finds, from the top, the bin where the running count reaches `need` (pass 1: need = k; pass 2:
+// what pass 1 left).  256 threads, thread i owns bins [i NB / 256, (i + 1) NB / 256).
+template <int NB>
+__device__ __forceinline__ void pick_bin(const int32_t* hist, int need, int* out_bin, int* out_left) {
+  __shared__ int wsum[4];
+  __shared__ int tot;
+  constexpr int per = NB / 256;
+  const int i = threadIdx.x;
+  // thread i takes bins counted from the top: (255 - i) per .. + per - 1, scanned top first
+  const int hi_bin = NB - 1 - i * per;
+  int mine = 0;
+  for (int j = 0; j < per; ++j) mine += hist[hi_bin - j];
+  const int incl = block_scan<256>(mine, wsum, &tot);
+  const int before = incl - mine;  // keys in the bins above this thread's range
+  if (before < need && incl >= need) {
+    int cum = before, d = hi_bin;
+    for (int j = 0; j < per; ++j, --d) {
+      if (cum + hist[d] >= need) break;
+      cum += hist[d];
+    }
+    *out_bin = d;
+    *out_left = need - cum;
+  }
+}
+
+__global__ __launch_bounds__(256) void topk_pick1_kernel(const int32_t* __restrict__ seq_lens, int k, TopkWs w) {
+  const int b = blockIdx.x;
+  const int n = max(seq_lens[b], 0);
+  int* pk = w.pick + 4 * b;
+  if (n <= k) {
+    if (threadIdx.x == 0) { pk[0] = -1; pk[1] = 0; pk[2] = -1; pk[3] = 0; }
+    return;
+  }
+  pick_bin<kBins1>(w.hist1 + (size_t)b * kBins1, k, &pk[0], &pk[1]);
+}
+
+// Histogram of the low key bits of the keys in the chosen high bin.
+__global__ __launch_bounds__(256) void topk_hist2_kernel(const int32_t* __restrict__ seq_lens, TopkWs w) {
+  __shared__ int hist[kBins2];
+  const int b = blockIdx.y;
+  const int len = seq_lens[b];
+  const int t0 = blockIdx.x * kChunk;
+  const int d1 = w.pick[4 * b];
+  if (d1 < 0 || t0 >= len) return;
+  for (int i = threadIdx.x; i < kBins2; i += 256) hist[i] = 0;
+  __syncthreads();
+  for (int t = t0 + threadIdx.x; t < min(t0 + kChunk, len); t += 256) {
+    const int key = key_of(w.scores[(size_t)b * w.stride + t]);
+    if ((key >> 11) == d1) atomicAdd(&hist[key & 2047], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins2; i += 256)
+    if (hist[i]) atomicAdd(&w.hist2[(size_t)b * kBins2 + i], hist[i]);
+}
+
+__global__ __launch_bounds__(256) void topk_pick2_kernel(TopkWs w) {
+  const int b = blockIdx.x;
+  int* pk = w.pick + 4 * b;
+  const int d1 = pk[0];
+  if (d1 < 0) return;
+  __shared__ int d2, left;
+  pick_bin<kBins2>(w.hist2 + (size_t)b * kBins2, pk[1], &d2, &left);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    pk[2] = (d1 << 11) | d2;
+    pk[3] = left;
+  }
+}
+
+// Per chunk: keys above the threshold and keys equal to it (every token counts as above when the
+// sequence keeps them all).
+__global__ __launch_bounds__(256) void topk_count_kernel(const int32_t* __restrict__ seq_lens, TopkWs w) {
+  __shared__ int red[2][4];
+  const int b = blockIdx.y;
+  const int c = blockIdx.x;
+  const int len = max(seq_lens[b], 0);
+  const int T = w.pick[4 * b + 2];
+  int gt = 0, eq = 0;
+  for (int t = c * kChunk + threadIdx.x; t < min((c + 1) * kChunk, len); t += 256) {
+    const int key = T < 0 ? 1 : key_of(w.scores[(size_t)b * w.stride + t]);
+    gt += key > T;
+    eq += key == T;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    gt += __shfl_xor(gt, o, 64);
+    eq += __shfl_xor(eq, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) { red[0][threadIdx.x >> 6] = gt; red[1][threadIdx.x >> 6] = eq; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t* ch = w.chunk + ((size_t)b * w.nchunks + c) * 2;
+    ch[0] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    ch[1] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  }
+}
+
+// Per sequence, in chunk order: (kept keys before the chunk, equal keys before the chunk), and the
+// count of kept tokens.  256 chunks at a time, each a thread, through two workgroup scans.
+__global__ __launch_bounds__(256) void topk_scan_kernel(const int32_t* __restrict__ seq_lens, int k, TopkWs w,
+                                                        int32_t* __restrict__ counts) {
+  __shared__ int wsum[4];
+  __shared__ int tot[2];
+  const int b = blockIdx.x;
+  const int len = max(seq_lens[b], 0);
+  const int need_eq = w.pick[4 * b + 3];
+  const int nch = (len + kChunk - 1) / kChunk;
+  int kept_base = 0, eq_base = 0;
+  for (int c0 = 0; c0 < nch; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    int32_t* ch = w.chunk + ((size_t)b * w.nchunks + c) * 2;
+    int gt = 0, eq = 0;
+    if (c < nch) {
+      gt = ch[0];
+      eq = ch[1];
+    }
+    const int eq_before = eq_base + block_scan<256>(eq, wsum, &tot[0]) - eq;
+    const int eq_total = tot[0];
+    const int kept = gt + min(max(need_eq - eq_before, 0), eq);
+    const int kept_before = kept_base + block_scan<256>(kept, wsum, &tot[1]) - kept;
+    const int kept_total = tot[1];
+    if (c < nch) {
+      ch[0] = kept_before;
+      ch[1] = eq_before;
+    }
+    kept_base += kept_total;
+    eq_base += eq_total;
+  }
+  if (threadIdx.x == 0) counts[b] = min(len, k);
+}
+
+// Writes the kept positions of chunk blockIdx.x in increasing order.
+__global__ __launch_bounds__(kChunk) void topk_write_kernel(const int32_t* __restrict__ seq_lens, int k, TopkWs w,
+                                                            int32_t* __restrict__ positions) {
+  __shared__ int wsum[kChunk / 64];
+  __shared__ int tot[2];
+  const int b = blockIdx.y;
+  const int c = blockIdx.x;
+  const int len = max(seq_lens[b], 0);
+  if (c * kChunk >= len) return;
+  const int T = w.pick[4 * b + 2], need_eq = w.pick[4 * b + 3];
+  const int32_t* ch = w.chunk + ((size_t)b * w.nchunks + c) * 2;
+  const int base = ch[0], eq_before = ch[1];
+  const int t = c * kChunk + threadIdx.x;
+  const int key = t < len ? (T < 0 ? 1 : key_of(w.scores[(size_t)b * w.stride + t])) : -2;
+  const int eq = (t < len && key == T) ? 1 : 0;
+  const int eq_rank = eq_before + block_scan<kChunk>(eq, wsum, &tot[0]) - 1;
+  const int take = (t < len && (key > T || (eq && eq_rank < need_eq))) ? 1 : 0;
+  const int at = base + block_scan<kChunk>(take, wsum, &tot[1]) - 1;
+  if (take) positions[(size_t)b * k + at] = t;
+}
+
+// Row i < counts[b] of sequence b: 72 lanes of 16 bytes from its page to compact page
+// b * P + i / 64, slot i % 64.  The first row's workgroup also writes the compact block table.
+__global__ __launch_bounds__(128) void gather_rows_kernel(const uint16_t* __restrict__ cache,
+                                                          const int32_t* __restrict__ block_table, int max_blocks,
+                                                          const int32_t* __restrict__ positions,
+                                                          const int32_t* __restrict__ counts, int k, int pk,
+                                                          uint16_t* __restrict__ out, int32_t* __restrict__ out_bt) {
+  const int i = blockIdx.x;
+  const int b = blockIdx.y;
+  const int c = threadIdx.x;
+  if (i == 0)
+    for (int j = c; j < pk; j += 128) out_bt[(size_t)b * pk + j] = b * pk + j;
+  if (c >= kRow / 8 || i >= counts[b]) return;
+  const int t = positions[(size_t)b * k + i];
+  const int page = block_table[(size_t)b * max_blocks + t / kPage];
+  const uint4 v = *reinterpret_cast<const uint4*>(cache + ((size_t)page * kPage + t % kPage) * kRow + 8 * c);
+  *reinterpret_cast<uint4*>(out + (((size_t)b * pk + i / kPage) * kPage + i % kPage) * kRow + 8 * c) = v;
+}
+
+}  // namespace
+
+static TopkWs topk_ws(void* base, int batch, int max_blocks) {
+  TopkWs w;
+  w.stride = max_blocks * kPage;
+  w.nchunks = (w.stride + kChunk - 1) / kChunk;
+  int32_t* p = static_cast<int32_t*>(base);
+  w.scores = p;
+  p += (size_t)batch * w.stride;
+  w.hist1 = p;
+  p += (size_t)batch * kBins1;
+  w.hist2 = p;
+  p += (size_t)batch * kBins2;
+  w.pick = p;
+  p += (size_t)batch * 4;
+  w.chunk = p;
+  return w;
+}
+
+size_t index_topk_workspace_bytes(int batch, int max_blocks) {
+  const size_t stride = (size_t)max_blocks * kPage;
+  const size_t nchunks = (stride + kChunk - 1) / kChunk;
+  return (size_t)batch * (stride + kBins1 + kBins2 + 4 + 2 * nchunks) * sizeof(int32_t);
+}
+
+hipError_t launch_index_topk(const int8_t* index_cache, const int32_t* block_table, int max_blocks,
+                             const int32_t* seq_lens, const int8_t* q_index, int batch, int k, int32_t* positions,
+                             int32_t* counts, void* workspace, hipStream_t s) {
+  const TopkWs w = topk_ws(workspace, batch, max_blocks);
+  const dim3 chunks(w.nchunks, batch);
+  hipLaunchKernelGGL(topk_clear_kernel, dim3(batch), dim3(256), 0, s, w);
+  hipLaunchKernelGGL(index_score_kernel, chunks, dim3(256), 0, s, index_cache, block_table, max_blocks, seq_lens,
+                     q_index, w);
+  hipLaunchKernelGGL(topk_pick1_kernel, dim3(batch), dim3(256), 0, s, seq_lens, k, w);
+  hipLaunchKernelGGL(topk_hist2_kernel, chunks, dim3(256), 0, s, seq_lens, w);
+  hipLaunchKernelGGL(topk_pick2_kernel, dim3(batch), dim3(256), 0, s, w);
+  hipLaunchKernelGGL(topk_count_kernel, chunks, dim3(256), 0, s, seq_lens, w);
+  hipLaunchKernelGGL(topk_scan_kernel, dim3(batch), dim3(256), 0, s, seq_lens, k, w, counts);
+  hipLaunchKernelGGL(topk_write_kernel, chunks, dim3(kChunk), 0, s, seq_lens, k, w, positions);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* cache, const int32_t* block_table, int max_blocks,
+                              const int32_t* positions, const int32_t* counts, int batch, int k, void* out,
+                              int32_t* out_bt, hipStream_t s) {
+  const int pk = (k + kPage - 1) / kPage;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(k, batch), dim3(128), 0, s, (const uint16_t*)cache, block_table,
+                     max_blocks, positions, counts, k, pk, (uint16_t*)out, out_bt);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -219,6 +219,34 @@ size_t mla_out_proj_hidden_workspace_size(int batch, int num_heads, mla_dtype dt
 mla_status mla_out_proj_hidden(const void* out, const void* w_o, void* hidden, int batch, int num_heads,
                                void* workspace, size_t workspace_bytes, mla_dtype dtype, hipStream_t stream);
 
+/*
+ * Attention over the top-k tokens of a cheap index ("DeepSeek (AI)" wiki, "KV cache data movement
+ * minimization": each token also carries a cheap index vector; the decode query scores them all,
+ * and attention reads only the k best rows).  The pages leave the index format open; here:
+ *   index_cache  int8 [num_pages][64][MLA_INDEX_DIM], paged like kv_cache (same block table)
+ *   q_index      int8 [batch][MLA_INDEX_DIM]: each sequence's index query
+ *   score_t      = q_index[b] . index_cache[token t], an exact integer, for t < seq_lens[b]
+ * mla_index_topk keeps the k highest scores of each sequence (ties to the earlier position; all
+ * tokens when seq_lens[b] <= k) and writes them to positions [batch][k] in increasing order, with
+ * counts[b] = min(k, seq_lens[b]) (entries past counts[b] untouched).  workspace: at least
+ * mla_index_topk_workspace_size(batch, max_blocks_per_seq) bytes (int32 scores).
+ * mla_gather_rows copies the kept rows of kv_cache into compact pages: sequence b's i-th kept row
+ * goes to page b * P + i / 64, slot i % 64 of out_cache [batch * P][64][576] (P = ceil(k / 64)),
+ * and out_block_table [batch][P] gets b * P + j; mla_decode over (out_cache, out_block_table,
+ * counts) is then the attention over the kept tokens.
+ * Errors: MLA_ERR_UNSUPPORTED unless page_size is 64; MLA_ERR_SHAPE for k < 1 or bad sizes;
+ * MLA_ERR_NULL, MLA_ERR_WORKSPACE; with MLA_DEBUG_CHECKS=1, MLA_ERR_BLOCK_TABLE as mla_decode.
+ */
+#define MLA_INDEX_DIM 128
+size_t mla_index_topk_workspace_size(int batch, int max_blocks_per_seq);
+mla_status mla_index_topk(const int8_t* index_cache, int num_pages, int page_size, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* seq_lens, const int8_t* q_index, int batch, int k,
+                          int32_t* positions, int32_t* counts, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+mla_status mla_gather_rows(const void* kv_cache, int num_pages, int page_size, const int32_t* block_table,
+                           int max_blocks_per_seq, const int32_t* positions, const int32_t* counts, int batch,
+                           int k, void* out_cache, int32_t* out_block_table, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

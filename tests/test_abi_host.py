@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.mla_abi_version() == 103
+    assert L.mla_abi_version() == 104
     for code, name in L.STATUS.items():
         assert L.mla_status_string(code).startswith(name)
     assert "unknown" in L.mla_status_string(12345)
@@ -199,3 +199,32 @@ def test_out_proj_hidden_validation_and_workspace():
     assert f(FAKE, FAKE, FAKE, 2, 128, None, ws, 0, None) == -4
     assert f(FAKE, FAKE, FAKE, 2, 128, FAKE, ws - 1, 0, None) == -4
     assert f(None, None, None, 0, 128, None, 0, 0, None) == 0
+
+
+def test_index_topk_and_gather_validation():
+    """Top-k path: workspace (per sequence: int32 scores for every block, 4,096 + 2,048 histogram
+    bins, 4 selection words, 2 words per 1,024-token chunk) and host validation."""
+    L = _lib()
+    assert L.INDEX_DIM == 128
+    assert L.mla_index_topk_workspace_size(4, 2049) == 4 * (2049 * 64 + 4096 + 2048 + 4 + 2 * 129) * 4
+    assert L.mla_index_topk_workspace_size(4, 0) == 0
+    t = L.lib.mla_index_topk
+    ws = 2 * (4 * 64 + 4096 + 2048 + 4 + 2 * 1) * 4
+    ok = [FAKE, 8, 64, FAKE, 4, FAKE, FAKE, 2, 16, FAKE, FAKE, FAKE, ws, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return t(*a)
+    assert t(*ok[:2], 32, *ok[3:]) == -5          # page size
+    assert call(8, 0) == -2                        # k
+    assert call(7, -1) == -2                       # batch
+    assert call(0, None) == -1
+    assert call(9, None) == -1
+    assert call(11, None) == -4
+    assert call(12, ws - 1) == -4
+    assert t(None, 0, 64, None, 4, None, None, 0, 16, None, None, None, 0, None) == 0
+    g = L.lib.mla_gather_rows
+    assert g(FAKE, 8, 64, FAKE, 4, FAKE, FAKE, 2, 0, FAKE, FAKE, None) == -2
+    assert g(FAKE, 8, 16, FAKE, 4, FAKE, FAKE, 2, 8, FAKE, FAKE, None) == -5
+    assert g(FAKE, 8, 64, FAKE, 4, FAKE, FAKE, 2, 8, None, FAKE, None) == -1
+    assert g(None, 0, 64, None, 4, None, None, 0, 8, None, None, None) == 0

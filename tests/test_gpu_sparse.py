@@ -1,0 +1,141 @@
+"""GPU parity of attention over the top-k tokens of a cheap int8 index, through the C ABI: the kept
+positions and counts bit for bit against the oracle (ragged lengths, short sequences, tie-heavy
+scores), the gathered rows byte for byte, and the decode over them within the bf16 tolerance, at
+small sizes and at 4 x 131,072 tokens with k = 2,048."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import mla_oracle as O
+from tests.gpu_cases import BF16_TOL, Gpu, host_inputs, pick, rel_err, say, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    import head_latent_attention_17_amd as L
+    return L
+
+
+def _topk(lib, wl, idx, qi, k, lens=None):
+    dev = "cuda"
+    bt = torch.as_tensor(wl.block_table, device=dev)
+    lens = torch.as_tensor(wl.attended_lens.astype(np.int32) if lens is None else lens, device=dev)
+    pos = torch.full((wl.batch, k), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((wl.batch,), -7, dtype=torch.int32, device=dev)
+    ws = torch.empty(lib.mla_index_topk_workspace_size(wl.batch, wl.max_blocks), dtype=torch.uint8, device=dev)
+    lib.mla_index_topk(idx, bt, lens, qi, k, pos, cnt, ws)
+    torch.cuda.synchronize()
+    return pos.cpu().numpy(), cnt.cpu().numpy()
+
+
+def _check_positions(wl, idx_np, qi_np, k, pos, cnt, seqs=None):
+    for b in (range(wl.batch) if seqs is None else seqs):
+        n = int(wl.attended_lens[b])
+        want = O.top_k_positions(O.index_scores(idx_np, wl.block_table, b, n, qi_np[b]), k)
+        assert cnt[b] == len(want), (b, cnt[b], len(want))
+        assert np.array_equal(pos[b, :len(want)], want), b
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 256])
+def test_topk_matches_oracle(lib, k):
+    wl = synth.make_custom([0, 1, 5, 64, 100, 1000, 5000], heads=16, seed=140 + k)
+    say("index top-k", k)
+    idx = synth.index_cache(wl, 0, device="cuda")
+    qi = synth.index_queries(wl, 0, device="cuda")
+    pos, cnt = _topk(lib, wl, idx, qi, k)
+    _check_positions(wl, idx.cpu().numpy(), qi.cpu().numpy(), k, pos, cnt)
+
+
+@pytest.mark.parametrize("levels", [1, 3])
+def test_topk_ties(lib, levels):
+    """Index vectors with entries in {0} or {-1, 0, 1}: all scores equal, or few distinct values, so
+    the tie rule (earlier position first) decides most of the selection."""
+    wl = synth.make_custom([300, 2000, 64], heads=16, seed=150 + levels)
+    say("index top-k ties", levels)
+    rng = np.random.default_rng(levels)
+    idx_np = (rng.integers(0, levels, (wl.num_pages, 64, 128)) - (levels // 2)).astype(np.int8)
+    qi_np = np.ones((wl.batch, 128), np.int8)
+    pos, cnt = _topk(lib, wl, torch.from_numpy(idx_np).cuda(), torch.from_numpy(qi_np).cuda(), 100)
+    _check_positions(wl, idx_np, qi_np, 100, pos, cnt)
+
+
+def _sparse_decode(lib, wl, k, g, cnt_dev, pos_dev):
+    dev = "cuda"
+    pk = -(-k // 64)
+    out_cache = torch.empty((wl.batch * pk, 64, 576), dtype=torch.bfloat16, device=dev)
+    out_bt = torch.full((wl.batch, pk), -1, dtype=torch.int32, device=dev)
+    lib.mla_gather_rows(g.cache, g.bt, pos_dev, cnt_dev, out_cache, out_bt)
+    ws = torch.empty(lib.mla_decode_workspace_size(wl.batch, wl.heads, pk, 0), dtype=torch.uint8, device=dev)
+    lib.mla_decode(g.q_lat_in, out_cache, out_bt, cnt_dev, wl.scale, g.o_lat, g.lse, ws)
+    torch.cuda.synchronize()
+    return out_cache, out_bt
+
+
+def test_gathered_rows_and_sparse_decode(lib):
+    """The gathered compact pages hold exactly the kept rows, and decode over them matches the
+    oracle's attention over the top-k tokens; a short sequence keeps all its tokens and an empty one
+    gives zeros."""
+    k = 256
+    wl = synth.make_custom([0, 40, 256, 700, 3000], heads=128, seed=160)
+    say("sparse decode", k)
+    g = Gpu(wl)
+    dev = "cuda"
+    idx = synth.index_cache(wl, 0, device=dev)
+    qi = synth.index_queries(wl, 0, device=dev)
+    bt = torch.as_tensor(wl.block_table, device=dev)
+    pos_dev = torch.zeros((wl.batch, k), dtype=torch.int32, device=dev)
+    cnt_dev = torch.zeros((wl.batch,), dtype=torch.int32, device=dev)
+    ws = torch.empty(lib.mla_index_topk_workspace_size(wl.batch, wl.max_blocks), dtype=torch.uint8, device=dev)
+    lib.mla_index_topk(idx, bt, g.attended, qi, k, pos_dev, cnt_dev, ws)
+    out_cache, out_bt = _sparse_decode(lib, wl, k, g, cnt_dev, pos_dev)
+    hi = host_inputs(wl, 0, range(wl.batch))
+    o_ref, lse_ref, chosen = O.sparse_latent_decode(hi["q_lat"], hi["cache"], wl.block_table, wl.attended_lens,
+                                                    idx.cpu().numpy(), qi.cpu().numpy(), k, wl.scale)
+    pk = -(-k // 64)
+    oc = synth.to_numpy_u16(out_cache.view(torch.int16))
+    assert np.array_equal(out_bt.cpu().numpy(), np.arange(wl.batch * pk).reshape(wl.batch, pk))
+    for b in range(wl.batch):
+        rows = hi["cache"][wl.block_table[b][chosen[b] // 64], chosen[b] % 64]
+        i = np.arange(len(chosen[b]))
+        assert np.array_equal(oc[b * pk + i // 64, i % 64], rows)
+    o = to_host_f64(g.o_lat)
+    assert torch.all(g.o_lat[0].float() == 0) and torch.all(torch.isneginf(g.lse[0]))
+    e_o = rel_err(o[1:], o_ref[1:])
+    lse = g.lse.cpu().numpy()
+    e_l = float(np.abs(lse[1:] - lse_ref[1:]).max() / np.abs(lse_ref[1:]).max())
+    say(f"  o_lat err {e_o:.3e}  lse err {e_l:.3e}")
+    assert e_o <= BF16_TOL and e_l <= BF16_TOL
+
+
+def test_full_size(lib):
+    """4 x 131,072 tokens (+1), k = 2,048: every sequence's kept positions bit for bit, and the
+    decode over them on sampled heads."""
+    import bench
+    wl = bench.bench_workload(3)
+    k = 2048
+    say("sparse full size", wl.name)
+    g = Gpu(wl)
+    dev = "cuda"
+    idx = synth.index_cache(wl, 0, device=dev)
+    qi = synth.index_queries(wl, 0, device=dev)
+    lib.mla_cache_append(g.cache, g.bt, g.lens, g.c_new, g.kpe_new)
+    pos, cnt = _topk(lib, wl, idx, qi, k)
+    idx_np, qi_np = idx.cpu().numpy(), qi.cpu().numpy()
+    _check_positions(wl, idx_np, qi_np, k, pos, cnt)
+    pos_dev = torch.from_numpy(pos).cuda()
+    cnt_dev = torch.from_numpy(cnt).cuda()
+    _sparse_decode(lib, wl, k, g, cnt_dev, pos_dev)
+    heads = pick(wl.heads, 4, 170)
+    seqs = [0, 3]
+    o = to_host_f64(g.o_lat)
+    hi = host_inputs(wl, 0, seqs)
+    o_ref, lse_ref, _ = O.sparse_latent_decode(hi["q_lat"], hi["cache"], wl.block_table, wl.attended_lens, idx_np,
+                                               qi_np, k, wl.scale, batch=seqs, heads=heads)
+    sel = np.ix_(seqs, heads)
+    e_o = rel_err(o[sel], o_ref[sel])
+    say(f"  o_lat err {e_o:.3e}")
+    assert e_o <= BF16_TOL
