@@ -10,9 +10,9 @@
 //   select    a two-pass radix select over many workgroups: the high bin holding the k-th largest
 //             key, then a 2,048-bin histogram of the low bits inside it, give the k-th largest key
 //             T and how many keys equal to T are kept (the earliest ones).
-//   write     per chunk, keys above T and equal to T are counted; one scan over the chunks gives
-//             each chunk its output offset; each chunk then writes its kept positions, so the
-//             result is in increasing position order.
+//   write     per chunk, keys above T and equal to T are counted; each chunk's output offset is
+//             the kept count of the chunks before it (two sums, since equal keys are kept in
+//             position order), and each chunk writes its kept positions, in increasing order.
 //   gather    copies the kept rows into compact pages (sequence b owns pages b P .. b P + P - 1,
 //             P = ceil(k / 64)) and writes their block table, so that mla_decode runs over them
 //             unchanged.
@@ -29,7 +29,7 @@ constexpr int kBins2 = 2048;          // key & 2047
 // Workspace layout (int32), per sequence b:
 //   scores [B][stride]; hist1 [B][4096]; hist2 [B][2048]; pick [B][4] (hi bin, left after it,
 //   threshold key T, keys equal to T to keep; T = -1 keeps every token); chunk [B][nchunks][2]
-//   (keys above T, keys equal to T) turned into (output offset, equal keys before the chunk).
+//   (keys above T, keys equal to T).
 struct TopkWs {
   int32_t* scores;
   int32_t* hist1;
@@ -62,23 +62,38 @@ __global__ __launch_bounds__(256) void index_score_kernel(const int8_t* __restri
   __syncthreads();
   const int part = threadIdx.x & 7;  // 16-byte part of the vector
   const int4 q = *reinterpret_cast<const int4*>(q_index + (size_t)b * kIndexDim + 16 * part);
-  for (int step = 0; step < kChunk / 32; ++step) {
-    const int t = t0 + step * 32 + (threadIdx.x >> 3);
-    int s = 0;
-    if (t < len) {
-      const int page = block_table[(size_t)b * max_blocks + t / kPage];
-      const int4 v = *reinterpret_cast<const int4*>(index_cache + ((size_t)page * kPage + t % kPage) * kIndexDim + 16 * part);
-      s = __builtin_amdgcn_sdot4(v.x, q.x, s, false);
-      s = __builtin_amdgcn_sdot4(v.y, q.y, s, false);
-      s = __builtin_amdgcn_sdot4(v.z, q.z, s, false);
-      s = __builtin_amdgcn_sdot4(v.w, q.w, s, false);
+  int32_t* __restrict__ scores = w.scores + (size_t)b * w.stride;
+  // eight steps of 32 tokens at a time: all their loads are issued before any score is stored
+  for (int s0 = 0; s0 < kChunk / 32; s0 += 8) {
+    int4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // a 32-token step lies inside one page (chunks start on page boundaries, two steps a page),
+      // so its page id is the same for the whole workgroup: a scalar load
+      const int step = s0 + u;
+      const int t = t0 + step * 32 + (threadIdx.x >> 3);
+      v[u] = make_int4(0, 0, 0, 0);
+      if (t0 + step * 32 < len) {
+        const int page = ((const __attribute__((address_space(4))) int32_t*)block_table)[(size_t)b * max_blocks + (t0 >> 6) + (step >> 1)];
+        if (t < len)
+          v[u] = *reinterpret_cast<const int4*>(index_cache + ((size_t)page * kPage + t % kPage) * kIndexDim + 16 * part);
+      }
     }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    s += __shfl_xor(s, 4, 64);
-    if (t < len && part == 0) {
-      w.scores[(size_t)b * w.stride + t] = s;
-      atomicAdd(&hist[key_of(s) >> 11], 1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + (s0 + u) * 32 + (threadIdx.x >> 3);
+      int sc = 0;
+      sc = __builtin_amdgcn_sdot4(v[u].x, q.x, sc, false);
+      sc = __builtin_amdgcn_sdot4(v[u].y, q.y, sc, false);
+      sc = __builtin_amdgcn_sdot4(v[u].z, q.z, sc, false);
+      sc = __builtin_amdgcn_sdot4(v[u].w, q.w, sc, false);
+      sc += __shfl_xor(sc, 1, 64);
+      sc += __shfl_xor(sc, 2, 64);
+      sc += __shfl_xor(sc, 4, 64);
+      if (t < len && part == 0) {
+        scores[t] = sc;
+        atomicAdd(&hist[key_of(sc) >> 11], 1);
+      }
     }
   }
   __syncthreads();
@@ -138,25 +153,25 @@ __device__ __forceinline__ void pick_bin(const int32_t* hist, int need, int* out
   }
 }
 
-__global__ __launch_bounds__(256) void topk_pick1_kernel(const int32_t* __restrict__ seq_lens, int k, TopkWs w) {
-  const int b = blockIdx.x;
-  const int n = max(seq_lens[b], 0);
+// Histogram of the low key bits of the keys in the high bin that holds the k-th largest key.
+// Every workgroup finds that bin from the high-bit histogram; the first one of each sequence
+// records it (bin, keys still needed inside it), or -1 when the sequence keeps every token.
+__global__ __launch_bounds__(256) void topk_hist2_kernel(const int32_t* __restrict__ seq_lens, int k, TopkWs w) {
+  __shared__ int hist[kBins2];
+  __shared__ int d1_s, left_s;
+  const int b = blockIdx.y;
+  const int len = max(seq_lens[b], 0);
+  const int t0 = blockIdx.x * kChunk;
   int* pk = w.pick + 4 * b;
-  if (n <= k) {
-    if (threadIdx.x == 0) { pk[0] = -1; pk[1] = 0; pk[2] = -1; pk[3] = 0; }
+  if (len <= k) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) { pk[0] = -1; pk[1] = 0; pk[2] = -1; pk[3] = 0; }
     return;
   }
-  pick_bin<kBins1>(w.hist1 + (size_t)b * kBins1, k, &pk[0], &pk[1]);
-}
-
-// Histogram of the low key bits of the keys in the chosen high bin.
-__global__ __launch_bounds__(256) void topk_hist2_kernel(const int32_t* __restrict__ seq_lens, TopkWs w) {
-  __shared__ int hist[kBins2];
-  const int b = blockIdx.y;
-  const int len = seq_lens[b];
-  const int t0 = blockIdx.x * kChunk;
-  const int d1 = w.pick[4 * b];
-  if (d1 < 0 || t0 >= len) return;
+  pick_bin<kBins1>(w.hist1 + (size_t)b * kBins1, k, &d1_s, &left_s);
+  __syncthreads();
+  const int d1 = d1_s;
+  if (blockIdx.x == 0 && threadIdx.x == 0) { pk[0] = d1; pk[1] = left_s; }
+  if (t0 >= len) return;
   for (int i = threadIdx.x; i < kBins2; i += 256) hist[i] = 0;
   __syncthreads();
   for (int t = t0 + threadIdx.x; t < min(t0 + kChunk, len); t += 256) {
@@ -168,28 +183,24 @@ __global__ __launch_bounds__(256) void topk_hist2_kernel(const int32_t* __restri
     if (hist[i]) atomicAdd(&w.hist2[(size_t)b * kBins2 + i], hist[i]);
 }
 
-__global__ __launch_bounds__(256) void topk_pick2_kernel(TopkWs w) {
-  const int b = blockIdx.x;
-  int* pk = w.pick + 4 * b;
-  const int d1 = pk[0];
-  if (d1 < 0) return;
-  __shared__ int d2, left;
-  pick_bin<kBins2>(w.hist2 + (size_t)b * kBins2, pk[1], &d2, &left);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    pk[2] = (d1 << 11) | d2;
-    pk[3] = left;
-  }
-}
-
-// Per chunk: keys above the threshold and keys equal to it (every token counts as above when the
-// sequence keeps them all).
+// Per chunk: keys above the k-th largest key T and keys equal to it (every token counts as above
+// when the sequence keeps them all).  Every workgroup finds T from the low-bit histogram; the first
+// one of each sequence records it with the number of keys equal to T that are kept.
 __global__ __launch_bounds__(256) void topk_count_kernel(const int32_t* __restrict__ seq_lens, TopkWs w) {
   __shared__ int red[2][4];
+  __shared__ int d2_s, left_s;
   const int b = blockIdx.y;
   const int c = blockIdx.x;
   const int len = max(seq_lens[b], 0);
-  const int T = w.pick[4 * b + 2];
+  int* pk = w.pick + 4 * b;
+  const int d1 = pk[0];
+  int T = -1;
+  if (d1 >= 0) {
+    pick_bin<kBins2>(w.hist2 + (size_t)b * kBins2, pk[1], &d2_s, &left_s);
+    __syncthreads();
+    T = (d1 << 11) | d2_s;
+    if (c == 0 && threadIdx.x == 0) { pk[2] = T; pk[3] = left_s; }
+  }
   int gt = 0, eq = 0;
   for (int t = c * kChunk + threadIdx.x; t < min((c + 1) * kChunk, len); t += 256) {
     const int key = T < 0 ? 1 : key_of(w.scores[(size_t)b * w.stride + t]);
@@ -210,52 +221,35 @@ __global__ __launch_bounds__(256) void topk_count_kernel(const int32_t* __restri
   }
 }
 
-// Per sequence, in chunk order: (kept keys before the chunk, equal keys before the chunk), and the
-// count of kept tokens.  256 chunks at a time, each a thread, through two workgroup scans.
-__global__ __launch_bounds__(256) void topk_scan_kernel(const int32_t* __restrict__ seq_lens, int k, TopkWs w,
-                                                        int32_t* __restrict__ counts) {
-  __shared__ int wsum[4];
-  __shared__ int tot[2];
-  const int b = blockIdx.x;
-  const int len = max(seq_lens[b], 0);
-  const int need_eq = w.pick[4 * b + 3];
-  const int nch = (len + kChunk - 1) / kChunk;
-  int kept_base = 0, eq_base = 0;
-  for (int c0 = 0; c0 < nch; c0 += 256) {
-    const int c = c0 + threadIdx.x;
-    int32_t* ch = w.chunk + ((size_t)b * w.nchunks + c) * 2;
-    int gt = 0, eq = 0;
-    if (c < nch) {
-      gt = ch[0];
-      eq = ch[1];
-    }
-    const int eq_before = eq_base + block_scan<256>(eq, wsum, &tot[0]) - eq;
-    const int eq_total = tot[0];
-    const int kept = gt + min(max(need_eq - eq_before, 0), eq);
-    const int kept_before = kept_base + block_scan<256>(kept, wsum, &tot[1]) - kept;
-    const int kept_total = tot[1];
-    if (c < nch) {
-      ch[0] = kept_before;
-      ch[1] = eq_before;
-    }
-    kept_base += kept_total;
-    eq_base += eq_total;
-  }
-  if (threadIdx.x == 0) counts[b] = min(len, k);
-}
-
-// Writes the kept positions of chunk blockIdx.x in increasing order.
+// Writes the kept positions of chunk blockIdx.x in increasing order.  Its output offset is the
+// number of kept keys in the earlier chunks: all their keys above T, plus min(keys equal to T that
+// are kept, keys equal to T in them), since the equal keys are kept in position order.
 __global__ __launch_bounds__(kChunk) void topk_write_kernel(const int32_t* __restrict__ seq_lens, int k, TopkWs w,
-                                                            int32_t* __restrict__ positions) {
+                                                            int32_t* __restrict__ positions,
+                                                            int32_t* __restrict__ counts) {
   __shared__ int wsum[kChunk / 64];
   __shared__ int tot[2];
   const int b = blockIdx.y;
   const int c = blockIdx.x;
   const int len = max(seq_lens[b], 0);
+  if (c == 0 && threadIdx.x == 0) counts[b] = min(len, k);
   if (c * kChunk >= len) return;
   const int T = w.pick[4 * b + 2], need_eq = w.pick[4 * b + 3];
-  const int32_t* ch = w.chunk + ((size_t)b * w.nchunks + c) * 2;
-  const int base = ch[0], eq_before = ch[1];
+  int gt_before = 0, eq_before = 0;
+  for (int c0 = 0; c0 < c; c0 += kChunk) {
+    const int cc = c0 + threadIdx.x;
+    int g = 0, e = 0;
+    if (cc < c) {
+      const int32_t* ch = w.chunk + ((size_t)b * w.nchunks + cc) * 2;
+      g = ch[0];
+      e = ch[1];
+    }
+    block_scan<kChunk>(g, wsum, &tot[0]);
+    gt_before += tot[0];
+    block_scan<kChunk>(e, wsum, &tot[1]);
+    eq_before += tot[1];
+  }
+  const int base = gt_before + min(need_eq, eq_before);
   const int t = c * kChunk + threadIdx.x;
   const int key = t < len ? (T < 0 ? 1 : key_of(w.scores[(size_t)b * w.stride + t])) : -2;
   const int eq = (t < len && key == T) ? 1 : 0;
@@ -317,12 +311,9 @@ hipError_t launch_index_topk(const int8_t* index_cache, const int32_t* block_tab
   hipLaunchKernelGGL(topk_clear_kernel, dim3(batch), dim3(256), 0, s, w);
   hipLaunchKernelGGL(index_score_kernel, chunks, dim3(256), 0, s, index_cache, block_table, max_blocks, seq_lens,
                      q_index, w);
-  hipLaunchKernelGGL(topk_pick1_kernel, dim3(batch), dim3(256), 0, s, seq_lens, k, w);
-  hipLaunchKernelGGL(topk_hist2_kernel, chunks, dim3(256), 0, s, seq_lens, w);
-  hipLaunchKernelGGL(topk_pick2_kernel, dim3(batch), dim3(256), 0, s, w);
+  hipLaunchKernelGGL(topk_hist2_kernel, chunks, dim3(256), 0, s, seq_lens, k, w);
   hipLaunchKernelGGL(topk_count_kernel, chunks, dim3(256), 0, s, seq_lens, w);
-  hipLaunchKernelGGL(topk_scan_kernel, dim3(batch), dim3(256), 0, s, seq_lens, k, w, counts);
-  hipLaunchKernelGGL(topk_write_kernel, chunks, dim3(kChunk), 0, s, seq_lens, k, w, positions);
+  hipLaunchKernelGGL(topk_write_kernel, chunks, dim3(kChunk), 0, s, seq_lens, k, w, positions, counts);
   return hipGetLastError();
 }
 
