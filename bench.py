@@ -381,7 +381,7 @@ def main():
         traffic_summary(*args.traffic_summary, bench_workload(args.config).name)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
