@@ -12,7 +12,8 @@ time), from K steps timed between two synchronisations with nothing else on the 
 `roofline` reports the dominant call, mla_decode, timed with HIP events on the launch stream in a
 second pass of the same K steps.
 `sparse_topk` times attention over each sequence's 2,048 best tokens of a cheap int8 index (scores and
-top-k, gather of the kept rows, decode over them) against the dense decode call.
+top-k, then the decode over the kept rows read in place; beside it the form that first gathers them
+into compact pages) against the dense decode call.
 `out_proj_hidden` times the projection of the step's per-head output to the hidden width through W^O.
 `producer` (workloads that append) times mla_cache_append_hidden, the producer side of the cache,
 graph-replayed over 48 weight copies.  `fp6` times mla_decode_fp6 over the ~6-bit form of the same
@@ -230,9 +231,11 @@ def out_hidden_timing(lib, synth, wl, dev, out, steps: int):
 
 def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_ms: float, k: int = 2048):
     """Attention over the top-k tokens of a cheap int8 index on the same workload: index scores and
-    top-k (mla_index_topk), the gather of the kept rows (mla_gather_rows) and the decode over them
-    (mla_decode), each stage between HIP events, `steps` times.  Algorithmic bytes = every token's
-    128-byte index vector + each kept row once (1,152 bytes)."""
+    top-k (mla_index_topk), then the decode over the kept tokens read in place (mla_decode_topk);
+    beside it the two-step form, the gather of the kept rows into compact pages (mla_gather_rows)
+    and mla_decode over them.  Each stage between HIP events, `steps` times; the two forms' outputs
+    are checked to agree bit for bit.  Algorithmic bytes = every token's 128-byte index vector +
+    each kept row once (1,152 bytes)."""
     import torch
     if wl.layers > 1:
         return None
@@ -246,20 +249,24 @@ def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_
     comp = torch.empty((B * pk, 64, ROW_ELEMS), dtype=torch.bfloat16, device=dev)
     comp_bt = torch.empty((B, pk), dtype=torch.int32, device=dev)
     ws_d = torch.empty(lib.mla_decode_workspace_size(B, H, pk, 0), dtype=torch.uint8, device=dev)
-    o_lat = torch.empty(B, H, D_C, dtype=torch.bfloat16, device=dev)
+    ws_i = torch.empty(lib.mla_decode_topk_workspace_size(B, H, k), dtype=torch.uint8, device=dev)
+    o_g = torch.empty(B, H, D_C, dtype=torch.bfloat16, device=dev)
+    o_i = torch.empty(B, H, D_C, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(B, H, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def run(ev=None):
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if ev is not None else None
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if ev is not None else None
         if marks: marks[0].record(stream)
         lib.mla_index_topk(idx, bt, att, qi, k, pos, cnt, ws_t)
         if marks: marks[1].record(stream)
         lib.mla_gather_rows(cache, bt, pos, cnt, comp, comp_bt)
         if marks: marks[2].record(stream)
-        lib.mla_decode(q_abs, comp, comp_bt, cnt, wl.scale, o_lat, lse, ws_d)
+        lib.mla_decode(q_abs, comp, comp_bt, cnt, wl.scale, o_g, lse, ws_d)
+        if marks: marks[3].record(stream)
+        lib.mla_decode_topk(q_abs, cache, bt, pos, cnt, wl.scale, o_i, lse, ws_i)
         if marks:
-            marks[3].record(stream)
+            marks[4].record(stream)
             ev.append(marks)
 
     for _ in range(3):
@@ -268,17 +275,24 @@ def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_
     for _ in range(steps):
         run(ev)
     torch.cuda.synchronize()
-    st = [sum(m[i].elapsed_time(m[i + 1]) for m in ev) / len(ev) for i in range(3)]
-    ms = sum(st)
+    if not torch.equal(o_g.view(torch.int16), o_i.view(torch.int16)):
+        raise SystemExit("mla_decode_topk differs from mla_gather_rows + mla_decode")
+    st = [sum(m[i].elapsed_time(m[i + 1]) for m in ev) / len(ev) for i in range(4)]
+    ms = st[0] + st[3]
+    ms_gather_path = st[0] + st[1] + st[2]
     kept = int(cnt.sum().item())
     nbytes = wl.tokens * 128 + kept * ROW_BYTES
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"calls": "mla_index_topk + mla_gather_rows + mla_decode", "k": k, "kept_tokens": kept,
+    return {"calls": "mla_index_topk + mla_decode_topk", "k": k, "kept_tokens": kept,
             "scored_tokens": wl.tokens, "ms_per_call": round(ms, 5),
-            "ms_topk": round(st[0], 5), "ms_gather": round(st[1], 5), "ms_decode": round(st[2], 5),
+            "ms_topk": round(st[0], 5), "ms_decode_topk": round(st[3], 5),
             "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "dense_decode_ms": round(dense_ms, 5),
-            "speedup_vs_dense": round(dense_ms / ms, 3)}
+            "speedup_vs_dense": round(dense_ms / ms, 3),
+            "gather_form": {"calls": "mla_index_topk + mla_gather_rows + mla_decode",
+                            "ms_per_call": round(ms_gather_path, 5), "ms_gather": round(st[1], 5),
+                            "ms_decode": round(st[2], 5),
+                            "speedup_vs_dense": round(dense_ms / ms_gather_path, 3)}}
 
 
 def cpu_baseline(wl, seconds: float):

@@ -22,7 +22,7 @@ EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", 
            "mla_absorb_q", "mla_decode", "mla_out_proj", "mla_cache_append_hidden_workspace_size",
            "mla_cache_append_hidden", "mla_cache_append_fp6", "mla_cache_quantize_fp6", "mla_decode_fp6",
            "mla_out_proj_hidden_workspace_size", "mla_out_proj_hidden", "mla_index_topk_workspace_size",
-           "mla_index_topk", "mla_gather_rows")
+           "mla_index_topk", "mla_gather_rows", "mla_decode_topk_workspace_size", "mla_decode_topk")
 INDEX_DIM = 128          # MLA_INDEX_DIM: int8 numbers in a token's index vector
 FP6_PAGE_BYTES = 27904   # MLA_FP6_PAGE_BYTES: 64 rows of 432 code bytes, then 64 float32 scales
 
@@ -66,6 +66,10 @@ lib.mla_index_topk.restype = _i
 lib.mla_index_topk.argtypes = [_p, _i, _i, _p, _i, _p, _p, _i, _i, _p, _p, _p, _sz, _p]
 lib.mla_gather_rows.restype = _i
 lib.mla_gather_rows.argtypes = [_p, _i, _i, _p, _i, _p, _p, _i, _i, _p, _p, _p]
+lib.mla_decode_topk_workspace_size.restype = _sz
+lib.mla_decode_topk_workspace_size.argtypes = [_i, _i, _i]
+lib.mla_decode_topk.restype = _i
+lib.mla_decode_topk.argtypes = [_p, _p, _i, _i, _p, _i, _p, _p, _i, _i, _i, _f, _p, _p, _p, _sz, _p]
 
 
 class MLAError(RuntimeError):
@@ -243,3 +247,20 @@ def mla_gather_rows(kv_cache, block_table, positions, counts, out_cache, out_blo
                                block_table.shape[1], _ptr(positions), _ptr(counts), positions.shape[0],
                                positions.shape[1], _ptr(out_cache), _ptr(out_block_table), _stream(stream)),
            "mla_gather_rows")
+
+
+def mla_decode_topk_workspace_size(batch: int, num_heads: int, k: int) -> int:
+    return int(lib.mla_decode_topk_workspace_size(batch, num_heads, k))
+
+
+def mla_decode_topk(q_abs, kv_cache, block_table, positions, counts, softmax_scale, o_lat, lse=None,
+                    workspace=None, stream=None):
+    """Attention over the kept tokens positions [B][k] (first counts[b] of each row) read in place:
+    q_abs [B][H][576] -> o_lat [B][H][512] and, if given, lse fp32 [B][H]; bf16 only."""
+    _dev(q_abs, kv_cache, block_table, positions, counts, o_lat, lse, workspace)
+    B, H = q_abs.shape[0], q_abs.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.mla_decode_topk(_ptr(q_abs), _ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1],
+                               _ptr(block_table), block_table.shape[1], _ptr(positions), _ptr(counts), B,
+                               positions.shape[1], H, float(softmax_scale), _ptr(o_lat), _ptr(lse),
+                               _ptr(workspace), ws_bytes, _stream(stream)), "mla_decode_topk")

@@ -289,20 +289,65 @@ __device__ __forceinline__ void dma16_group(const char* gbase, unsigned voff, un
   }
 }
 
+// The same copy from a per-lane 64-bit address: lane l's 16 bytes from addr + 128 j land at LDS byte
+// lds + 16 l (lds the block's own address; M0 takes lds - 128 j).  j must fold to a constant.
+__device__ __forceinline__ void dma16_addr(uint64_t addr, unsigned lds, int j) {
+  if (j == 0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(addr), "s"(lds)
+                 : "memory", "m0");
+  } else {
+    asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%3"
+                 :
+                 : "v"(addr), "s"(lds), "i"(-128 * j), "i"(128 * j)
+                 : "memory", "m0", "scc");
+  }
+}
+
+// Kept tokens read in place: the byte address of the cache row of list entry
+// min(8 g + tl, nt - 1) of the tile at cursor c (entries are token positions, read through the
+// block table).  The 16 list and table reads are wave-uniform scalar loads; each lane then selects
+// the row of its token-in-group tl.
+__device__ __forceinline__ uint64_t topk_row_addr(const DecodeParams& p, const TileCursor& c, int g, int nt,
+                                                  int tl) {
+  const size_t lb = (size_t)c.b * p.pos_stride + c.t;
+  const size_t tb = (size_t)c.b * p.max_blocks;
+  int r = 0;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const unsigned pos = (unsigned)ld_const(p.positions, lb + min(8 * g + kk, nt - 1));
+    const int row = ld_const(p.block_table, tb + pos / kPage) * kPage + (int)(pos % kPage);
+    r = (kk == 0 || tl == kk) ? row : r;
+  }
+  return (uint64_t)(uintptr_t)p.cache + (uint64_t)(unsigned)r * (kRow * 2);
+}
+
 // DMA of one tile: wave w fills blocks [w * per, (w + 1) * per).  For a full tile the per-lane part
 // of every source address is one of two lane constants (token-group parity); a ragged tile (fewer
 // than 32 tokens) re-reads its last valid row in place of the missing ones.
-template <int NW>
+template <int NW, bool TOPK>
 __device__ __forceinline__ void issue_tile(const DecodeParams& p, const TileCursor& c,
                                            LDS_AS char* stage, int wave) {
   constexpr int kPer = kBlocks / NW;
-  const int page = ld_const(p.block_table, (size_t)c.b * p.max_blocks + (unsigned)c.t / kPage);
   const int nt = min(kTileTok, c.t_end - c.t);
-  const char* base = reinterpret_cast<const char*>(p.cache) +
-                     ((size_t)page * kPage + ((unsigned)c.t % kPage)) * (kRow * 2);
   const unsigned lds = (unsigned)(uintptr_t)stage;
   int ln;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  if constexpr (TOPK) {  // the wave's token groups, each lane's row looked up through the list
+#pragma unroll
+    for (int g = 0; g < kPer / kCG; ++g) {
+      const int tg = wave * (kPer / kCG) + g;
+      const int tl = (ln >> 3) ^ (tg & 1);
+      const uint64_t ra = topk_row_addr(p, c, tg, nt, tl) + (unsigned)(((ln & 7) ^ sigma(tl)) * 16);
+#pragma unroll
+      for (int cg = 0; cg < kCG; ++cg) dma16_addr(ra, lds + (tg * kCG + cg) * 1024, cg);
+    }
+    return;
+  }
+  const int page = ld_const(p.block_table, (size_t)c.b * p.max_blocks + (unsigned)c.t / kPage);
+  const char* base = reinterpret_cast<const char*>(p.cache) +
+                     ((size_t)page * kPage + ((unsigned)c.t % kPage)) * (kRow * 2);
   if (nt == kTileTok) {
     // slot (lane / 8, lane % 8) of a block holds token-in-group (lane / 8) ^ parity and
     // chunk-in-group (lane % 8) ^ sigma(token-in-group)
@@ -479,8 +524,9 @@ __device__ __forceinline__ int xcd_unit(int id, int n) {
   return x * per + min(x, rem) + id / 8;
 }
 
-template <int NW, bool FP6>
+template <int NW, bool FP6, bool TOPK>
 __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p) {
+  static_assert(!(FP6 && TOPK), "kept tokens are read from bf16 rows");
   constexpr int kPer = kBlocks / NW;  // copies per wave per tile
   using G6 = Fp6Geom<NW>;
   __shared__ __attribute__((aligned(1024))) char ring[FP6 ? 3 : kStages][kTileBytes];
@@ -563,7 +609,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s) {
       if (ld.valid) {
-        issue_tile<NW>(p, ld, (LDS_AS char*)ring[s], wave);
+        issue_tile<NW, TOPK>(p, ld, (LDS_AS char*)ring[s], wave);
         ld.advance();
         ++issued;
       }
@@ -592,7 +638,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   // Refills the stage of the tile before `t` (every wave is past it) with the next tile.
   auto refill = [&](int t) __attribute__((always_inline)) {
     if (ld.valid) {
-      issue_tile<NW>(p, ld, (LDS_AS char*)ring[stg(t + kStages - 1)], wave);
+      issue_tile<NW, TOPK>(p, ld, (LDS_AS char*)ring[stg(t + kStages - 1)], wave);
       ld.advance();
       ++issued;
     }
@@ -669,6 +715,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // The ~6-bit cache copies a twelfth of the bytes per wave and issues them all at once.
       const char* sp_base = reinterpret_cast<const char*>(p.cache);
       unsigned sp_lane = 0, sp_lds = 0;
+      uint64_t sp_addr = 0;  // kept tokens: this lane's full source address
       int sp_page = 0, sp_tok = 0;
       bool sp_have = false;
       if constexpr (FP6) {
@@ -696,14 +743,19 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         const unsigned cl16 = (unsigned)((ln & 7) ^ sigma(tl)) * 16u;
         sp_have = ld.valid;
         if (ld.valid) {
-          sp_page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage);
-          sp_tok = (int)((unsigned)ld.t % kPage);
           const int ntl = min(kTileTok, ld.t_end - ld.t);
-          sp_lane = (unsigned)min(8 * wave + tl, ntl - 1) * (kRow * 2) + cl16;
+          if constexpr (TOPK) {
+            sp_addr = topk_row_addr(p, ld, wave, ntl, tl) + cl16;
+          } else {
+            sp_page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage);
+            sp_tok = (int)((unsigned)ld.t % kPage);
+            sp_lane = (unsigned)min(8 * wave + tl, ntl - 1) * (kRow * 2) + cl16;
+          }
           sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it + kStages - 1)] + wave * kPer * 1024;
           ld.advance();
         } else {
           sp_lane = (unsigned)(8 * wave + tl) * (kRow * 2) + cl16;
+          sp_addr = (uint64_t)(uintptr_t)sp_base + sp_lane;
           sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)sink;
         }
       }
@@ -711,7 +763,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // tile it - 1.
       if constexpr (!FP6) {
         tile_ready(last ? it : it + 1);
-        if constexpr (NW == 4) {
+        if constexpr (NW == 4 && TOPK) {
+          ++issued;
+          asm volatile("" : "+v"(sp_addr));
+        } else if constexpr (NW == 4) {
           ++issued;
           asm volatile("" : "+s"(sp_page));  // the page is first needed here, behind the wait
           if (sp_have) sp_base += ((size_t)sp_page * kPage + sp_tok) * (kRow * 2);
@@ -720,7 +775,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         }
       }
       auto spread_copy = [&](int j) __attribute__((always_inline)) {
-        if constexpr (NW == 4 && !FP6) dma16_group(sp_base, sp_lane, sp_lds, j);
+        if constexpr (NW == 4 && TOPK) dma16_addr(sp_addr, sp_lds + 1024 * j, j);
+        else if constexpr (NW == 4 && !FP6) dma16_group(sp_base, sp_lane, sp_lds, j);
       };
       // ~6-bit cache: copy j of tile it + 4 (spread over the score product like the bf16 copies)
       auto copy6 = [&](int j) __attribute__((always_inline)) {
@@ -939,19 +995,29 @@ bool mfma_supported(const DecodeParams& p) { return p.heads == 128 || p.heads ==
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
   if (p.fp6) {
+    if (p.positions) return hipErrorNotSupported;
     // No one-wave variant: with its conversion the compiler keeps that kernel's output accumulators
     // in memory across the tile loop, which the unpadded MFMA wrappers above do not allow.
     switch (p.heads) {
-      case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, true>), dim3(p.num_units), dim3(256), 0, s, p); break;
-      case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, true>), dim3(p.num_units), dim3(128), 0, s, p); break;
+      case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, true, false>), dim3(p.num_units), dim3(256), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, true, false>), dim3(p.num_units), dim3(128), 0, s, p); break;
+      default: return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+  }
+  if (p.positions) {
+    switch (p.heads) {
+      case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false, true>), dim3(p.num_units), dim3(256), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false, true>), dim3(p.num_units), dim3(128), 0, s, p); break;
+      case 32: hipLaunchKernelGGL((decode_mfma_kernel<1, false, true>), dim3(p.num_units), dim3(64), 0, s, p); break;
       default: return hipErrorNotSupported;
     }
     return hipGetLastError();
   }
   switch (p.heads) {
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false>), dim3(p.num_units), dim3(256), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false>), dim3(p.num_units), dim3(128), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<1, false>), dim3(p.num_units), dim3(64), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false, false>), dim3(p.num_units), dim3(256), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false, false>), dim3(p.num_units), dim3(128), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<1, false, false>), dim3(p.num_units), dim3(64), 0, s, p); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

@@ -58,7 +58,7 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_abi_version(void) { return 104; }
+int mla_abi_version(void) { return 105; }
 
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype) {
@@ -175,6 +175,8 @@ static mla_status decode_common(const void* q_abs, const void* kv_cache, int num
   p.ws_ml = p.ws_o + ((size_t)units + batch) * num_heads * kDc;
   p.seq_units = reinterpret_cast<int*>(p.ws_ml + ((size_t)units + batch) * num_heads * 2);
   p.fp6 = fp6 ? 1 : 0;
+  p.positions = nullptr;
+  p.pos_stride = 0;
   p.num_pages = num_pages;
   p.max_blocks = max_blocks_per_seq;
   p.batch = batch;
@@ -292,6 +294,61 @@ mla_status mla_gather_rows(const void* kv_cache, int num_pages, int page_size, c
   if (!kv_cache || !block_table || !positions || !counts || !out_cache || !out_block_table) return MLA_ERR_NULL;
   hipError_t e = launch_gather_rows(kv_cache, block_table, max_blocks_per_seq, positions, counts, batch, k, out_cache,
                                     out_block_table, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_decode_topk_workspace_size(int batch, int num_heads, int k) {
+  if (batch < 0 || k < 1 || !valid_heads(num_heads)) return 0;
+  const int kept_pages = (int)(((long long)k + kPage - 1) / kPage);
+  return workspace_bytes(batch, num_heads, auto_units(batch, num_heads, kept_pages));
+}
+
+mla_status mla_decode_topk(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                           const int32_t* block_table, int max_blocks_per_seq, const int32_t* positions,
+                           const int32_t* counts, int batch, int k, int num_heads, float softmax_scale,
+                           void* o_lat, float* lse, void* workspace, size_t workspace_bytes_given,
+                           hipStream_t stream) {
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (!valid_heads(num_heads)) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1 || k < 1) return MLA_ERR_SHAPE;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return MLA_ERR_SHAPE;
+  if (num_heads < 32) return MLA_ERR_UNSUPPORTED;  // matrix-core kernel only
+  if (batch == 0) return MLA_OK;
+  if (num_pages < 1) return MLA_ERR_SHAPE;
+  if (!q_abs || !kv_cache || !block_table || !positions || !counts || !o_lat) return MLA_ERR_NULL;
+  const int kept_pages = (int)(((long long)k + kPage - 1) / kPage);
+  const int units = auto_units(batch, num_heads, kept_pages);
+  const size_t need = workspace_bytes(batch, num_heads, units);
+  if (!workspace || workspace_bytes_given < need) return MLA_ERR_WORKSPACE;
+  if (debug_checks_enabled()) {
+    bool bad = false;
+    if (check_positions(block_table, max_blocks_per_seq, positions, counts, batch, k, num_pages, stream, &bad) !=
+        hipSuccess)
+      return MLA_ERR_HIP;
+    if (bad) return MLA_ERR_BLOCK_TABLE;
+  }
+
+  DecodeParams p;
+  p.q_abs = q_abs;
+  p.cache = static_cast<const uint16_t*>(kv_cache);
+  p.block_table = block_table;
+  p.seq_lens = counts;  // each sequence's list of kept tokens is what it attends to
+  p.o_lat = o_lat;
+  p.lse = lse;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + ((size_t)units + batch) * num_heads * kDc;
+  p.seq_units = reinterpret_cast<int*>(p.ws_ml + ((size_t)units + batch) * num_heads * 2);
+  p.fp6 = 0;
+  p.positions = positions;
+  p.pos_stride = k;
+  p.num_pages = num_pages;
+  p.max_blocks = max_blocks_per_seq;
+  p.batch = batch;
+  p.heads = num_heads;
+  p.num_units = units;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.partial_bf16 = 0;
+  hipError_t e = launch_decode(p, false, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

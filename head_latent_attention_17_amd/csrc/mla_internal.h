@@ -35,6 +35,11 @@ struct DecodeParams {
   int partial_bf16;    // 0: fp32 un-normalised sums; 1: bf16 sums already divided by the
                        // softmax sum, in the first half of each slot (set by launch_decode)
   int fp6;            // 1: cache holds ~6-bit pages (kFp6PageBytes each), 0: bf16 rows
+  // Attention over kept tokens in place (null: every token): sequence b attends to the tokens at
+  // positions[b * pos_stride + i], i < seq_lens[b] (here the kept counts), each read through the
+  // block table; its pages are then runs of 64 list entries.
+  const int32_t* positions;
+  int pos_stride;
   int num_pages;
   int max_blocks;
   int batch;
@@ -81,6 +86,10 @@ hipError_t launch_gather_rows(const void* cache, const int32_t* block_table, int
                               int32_t* out_bt, hipStream_t s);
 size_t index_topk_workspace_bytes(int batch, int max_blocks);
 
+// Device-side check of kept-token lists: counts[b] in [0, k], every listed position inside the
+// table row and naming a page in [0, num_pages); synchronises s.
+hipError_t check_positions(const int32_t* block_table, int max_blocks, const int32_t* positions,
+                           const int32_t* counts, int batch, int k, int num_pages, hipStream_t s, bool* bad);
 // Device-side check of block-table entries and lengths (append = false) or append positions
 // (append = true); synchronises s.  *bad is set when an entry is out of range.
 hipError_t check_tables(const int32_t* block_table, int max_blocks, const int32_t* lens, int batch,

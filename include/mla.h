@@ -247,6 +247,27 @@ mla_status mla_gather_rows(const void* kv_cache, int num_pages, int page_size, c
                            int max_blocks_per_seq, const int32_t* positions, const int32_t* counts, int batch,
                            int k, void* out_cache, int32_t* out_block_table, hipStream_t stream);
 
+/*
+ * Attention over the kept tokens read in place (same passage): the result of mla_gather_rows
+ * followed by mla_decode over the compact pages, bit for bit, without copying the rows.  Sequence b
+ * attends to the tokens at positions[b][0 .. counts[b]) (positions [batch][k] and counts [batch]
+ * as mla_index_topk writes them; any token positions in list order are allowed), each row read
+ * through block_table as mla_decode reads it.  counts[b] = 0 gives o_lat = 0 and lse = -inf.
+ * q_abs, o_lat, lse and scale as for mla_decode; bf16 only; num_heads in {32, 64, 128}.
+ * workspace: at least mla_decode_topk_workspace_size(batch, num_heads, k) bytes, contents
+ * irrelevant, used only during the call.  Counts and positions are trusted on the fast path; with
+ * MLA_DEBUG_CHECKS=1 a count above k, a position outside the table row or a table entry outside
+ * [0, num_pages) returns MLA_ERR_BLOCK_TABLE, launching nothing else.
+ * Errors: MLA_ERR_UNSUPPORTED (page_size != 64, num_heads not in {32, 64, 128}), MLA_ERR_SHAPE (k < 1,
+ * negative sizes, num_pages < 1 with batch > 0, scale not finite and positive), MLA_ERR_NULL,
+ * MLA_ERR_WORKSPACE, MLA_ERR_HIP.
+ */
+size_t mla_decode_topk_workspace_size(int batch, int num_heads, int k);
+mla_status mla_decode_topk(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                           const int32_t* block_table, int max_blocks_per_seq, const int32_t* positions,
+                           const int32_t* counts, int batch, int k, int num_heads, float softmax_scale,
+                           void* o_lat, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.mla_abi_version() == 104
+    assert L.mla_abi_version() == 105
     for code, name in L.STATUS.items():
         assert L.mla_status_string(code).startswith(name)
     assert "unknown" in L.mla_status_string(12345)
@@ -228,3 +228,36 @@ def test_index_topk_and_gather_validation():
     assert g(FAKE, 8, 16, FAKE, 4, FAKE, FAKE, 2, 8, FAKE, FAKE, None) == -5
     assert g(FAKE, 8, 64, FAKE, 4, FAKE, FAKE, 2, 8, None, FAKE, None) == -1
     assert g(None, 0, 64, None, 4, None, None, 0, 8, None, None, None) == 0
+
+
+def test_decode_topk_validation():
+    """In-place top-k decode: its workspace is that of mla_decode over compact pages of the kept
+    rows (ceil(k / 64) pages per sequence), and host validation runs before any launch."""
+    L = _lib()
+    for b, h, k in ((4, 128, 2048), (32, 128, 2048), (3, 64, 100), (1, 32, 1)):
+        assert L.mla_decode_topk_workspace_size(b, h, k) == L.mla_decode_workspace_size(b, h, -(-k // 64), 0)
+    assert L.mla_decode_topk_workspace_size(4, 128, 0) == 0
+    assert L.mla_decode_topk_workspace_size(4, 48, 64) == 0
+    f = L.lib.mla_decode_topk
+    ws = L.mla_decode_topk_workspace_size(2, 128, 100)
+    ok = [FAKE, FAKE, 8, 64, FAKE, 4, FAKE, FAKE, 2, 100, 128, 0.1, FAKE, None, FAKE, ws, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(3, 32) == -5                       # page size
+    assert call(10, 16) == -5                      # no matrix-core kernel for 16 heads
+    assert call(10, 48) == -5
+    assert call(9, 0) == -2                        # k
+    assert call(8, -1) == -2                       # batch
+    assert call(11, 0.0) == -2                     # scale
+    assert call(11, float("nan")) == -2
+    assert call(2, 0) == -2                        # empty cache with sequences to attend
+    assert call(0, None) == -1
+    assert call(6, None) == -1                     # positions
+    assert call(7, None) == -1                     # counts
+    assert call(12, None) == -1
+    assert call(14, None) == -4
+    assert call(15, ws - 1) == -4
+    assert f(None, None, 0, 64, None, 4, None, None, 0, 100, 128, 0.1, None, None, None, 0, None) == 0
+

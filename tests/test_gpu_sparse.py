@@ -1,7 +1,8 @@
 """GPU parity of attention over the top-k tokens of a cheap int8 index, through the C ABI: the kept
 positions and counts bit for bit against the oracle (ragged lengths, short sequences, tie-heavy
 scores), the gathered rows byte for byte, and the decode over them within the bf16 tolerance, at
-small sizes and at 4 x 131,072 tokens with k = 2,048."""
+small sizes and at 4 x 131,072 tokens with k = 2,048.  The in-place decode over the kept tokens
+(mla_decode_topk) must equal gather + decode bit for bit, and the oracle within the tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -139,3 +140,138 @@ def test_full_size(lib):
     e_o = rel_err(o[sel], o_ref[sel])
     say(f"  o_lat err {e_o:.3e}")
     assert e_o <= BF16_TOL
+
+
+def _topk_inplace(lib, wl, g, pos_dev, cnt_dev):
+    o = torch.empty_like(g.o_lat)
+    lse = torch.empty_like(g.lse)
+    k = pos_dev.shape[1]
+    ws = torch.empty(lib.mla_decode_topk_workspace_size(wl.batch, wl.heads, k), dtype=torch.uint8,
+                     device=pos_dev.device)
+    lib.mla_decode_topk(g.q_lat_in, g.cache, g.bt, pos_dev, cnt_dev, wl.scale, o, lse, ws)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _same_bits(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16)) if a.dtype == torch.bfloat16 else \
+        torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def _oracle_list_decode(hi, wl, pos, cnt, seqs, heads):
+    """The oracle's latent attention over the listed tokens of each chosen sequence."""
+    o = np.full((wl.batch, wl.heads, 512), np.nan)
+    lse = np.full((wl.batch, wl.heads), np.nan)
+    q = O.bf16_to_f64(hi["q_lat"])
+    for b in seqs:
+        p_b = pos[b, :cnt[b]]
+        pg, sl = O.page_and_slot(wl.block_table, b, p_b, 64)
+        rows = O.bf16_to_f64(hi["cache"][pg, sl]) if len(p_b) else np.zeros((0, 576))
+        for h in heads:
+            o[b, h], lse[b, h], _ = O.latent_attention(q[b, h], rows, 512, wl.scale)
+    return o, lse
+
+
+@pytest.mark.parametrize("heads,k", [(128, 100), (128, 256), (64, 7), (64, 100), (32, 256)])
+def test_decode_topk_matches_gather(lib, heads, k):
+    """mla_decode_topk over mla_index_topk's lists equals mla_gather_rows + mla_decode bit for bit
+    (empty, short, ragged and long sequences), and the oracle within the bf16 tolerance."""
+    wl = synth.make_custom([0, 1, 40, 256, 700, 3000], heads=heads, seed=180 + heads + k)
+    say("in-place top-k decode", heads, k)
+    g = Gpu(wl)
+    dev = "cuda"
+    idx = synth.index_cache(wl, 0, device=dev)
+    qi = synth.index_queries(wl, 0, device=dev)
+    pos_dev = torch.zeros((wl.batch, k), dtype=torch.int32, device=dev)
+    cnt_dev = torch.zeros((wl.batch,), dtype=torch.int32, device=dev)
+    ws = torch.empty(lib.mla_index_topk_workspace_size(wl.batch, wl.max_blocks), dtype=torch.uint8, device=dev)
+    lib.mla_index_topk(idx, g.bt, g.attended, qi, k, pos_dev, cnt_dev, ws)
+    o, lse = _topk_inplace(lib, wl, g, pos_dev, cnt_dev)
+    _sparse_decode(lib, wl, k, g, cnt_dev, pos_dev)
+    assert _same_bits(o, g.o_lat) and _same_bits(lse, g.lse)
+    assert torch.all(o[0].float() == 0) and torch.all(torch.isneginf(lse[0]))
+    seqs = range(1, wl.batch)
+    hd = pick(heads, 8, 190)
+    hi = host_inputs(wl, 0, seqs)
+    o_ref, lse_ref = _oracle_list_decode(hi, wl, pos_dev.cpu().numpy(), cnt_dev.cpu().numpy(), seqs, hd)
+    sel = np.ix_(list(seqs), hd)
+    e_o = rel_err(to_host_f64(o)[sel], o_ref[sel])
+    lse_np = lse.cpu().numpy()
+    e_l = float(np.abs(lse_np[sel] - lse_ref[sel]).max() / np.abs(lse_ref[sel]).max())
+    say(f"  o_lat err {e_o:.3e}  lse err {e_l:.3e}")
+    assert e_o <= BF16_TOL and e_l <= BF16_TOL
+
+
+def test_decode_topk_arbitrary_lists(lib):
+    """Any list of positions is attended in list order: unsorted lists with repeats and counts from
+    0 to k, against gather + decode bit for bit and the oracle over the same lists."""
+    k = 150
+    wl = synth.make_custom([5, 90, 600, 2000, 64, 1000, 333], heads=64, seed=200)
+    say("in-place top-k decode, arbitrary lists", k)
+    g = Gpu(wl)
+    rng = np.random.default_rng(201)
+    pos = np.full((wl.batch, k), -1, np.int32)            # entries past the count are never read
+    cnt = np.array([3, 0, 150, 149, 64, 97, 33], np.int32)
+    for b in range(wl.batch):
+        pos[b, :cnt[b]] = rng.integers(0, int(wl.attended_lens[b]), cnt[b])
+    pos_dev, cnt_dev = torch.from_numpy(pos).cuda(), torch.from_numpy(cnt).cuda()
+    o, lse = _topk_inplace(lib, wl, g, pos_dev, cnt_dev)
+    _sparse_decode(lib, wl, k, g, cnt_dev, pos_dev)
+    assert _same_bits(o, g.o_lat) and _same_bits(lse, g.lse)
+    seqs = [b for b in range(wl.batch) if cnt[b] > 0]
+    hi = host_inputs(wl, 0, seqs)
+    hd = pick(64, 8, 202)
+    o_ref, lse_ref = _oracle_list_decode(hi, wl, pos, cnt, seqs, hd)
+    sel = np.ix_(seqs, hd)
+    e_o = rel_err(to_host_f64(o)[sel], o_ref[sel])
+    say(f"  o_lat err {e_o:.3e}")
+    assert e_o <= BF16_TOL
+    assert torch.all(o[1].float() == 0) and torch.all(torch.isneginf(lse[1]))
+
+
+def test_decode_topk_debug_checks(lib, monkeypatch):
+    """MLA_DEBUG_CHECKS=1: valid lists give the unchecked result bit for bit; a count above k or a
+    position outside the table row is reported as MLA_ERR_BLOCK_TABLE before any decode launch."""
+    k = 64
+    wl = synth.make_custom([100, 300], heads=128, seed=210)
+    say("in-place top-k decode, debug checks")
+    g = Gpu(wl)
+    # valid lists: every position inside its own sequence (the unchecked call trusts them)
+    pos = np.stack([(np.arange(k) * 3) % int(n) for n in wl.attended_lens]).astype(np.int32)
+    cnt = np.array([k, 20], np.int32)
+    assert all((pos[b, :cnt[b]] < wl.attended_lens[b]).all() for b in range(wl.batch))
+    pos_dev, cnt_dev = torch.from_numpy(pos).cuda(), torch.from_numpy(cnt).cuda()
+    o0, lse0 = _topk_inplace(lib, wl, g, pos_dev, cnt_dev)
+    monkeypatch.setenv("MLA_DEBUG_CHECKS", "1")
+    o1, lse1 = _topk_inplace(lib, wl, g, pos_dev, cnt_dev)
+    assert _same_bits(o0, o1) and _same_bits(lse0, lse1)
+    bad_cnt = torch.tensor([k + 1, 20], dtype=torch.int32, device="cuda")
+    with pytest.raises(lib.MLAError) as e:
+        _topk_inplace(lib, wl, g, pos_dev, bad_cnt)
+    assert e.value.status == -6
+    bad_pos = pos.copy()
+    bad_pos[1, 5] = wl.max_blocks * 64
+    with pytest.raises(lib.MLAError) as e:
+        _topk_inplace(lib, wl, g, torch.from_numpy(bad_pos).cuda(), cnt_dev)
+    assert e.value.status == -6
+
+
+def test_decode_topk_full_size(lib):
+    """4 x 131,072 tokens (+1), k = 2,048: the in-place decode equals gather + decode bit for bit."""
+    import bench
+    wl = bench.bench_workload(3)
+    k = 2048
+    say("in-place top-k decode full size", wl.name)
+    g = Gpu(wl)
+    dev = "cuda"
+    idx = synth.index_cache(wl, 0, device=dev)
+    qi = synth.index_queries(wl, 0, device=dev)
+    lib.mla_cache_append(g.cache, g.bt, g.lens, g.c_new, g.kpe_new)
+    pos_dev = torch.zeros((wl.batch, k), dtype=torch.int32, device=dev)
+    cnt_dev = torch.zeros((wl.batch,), dtype=torch.int32, device=dev)
+    ws = torch.empty(lib.mla_index_topk_workspace_size(wl.batch, wl.max_blocks), dtype=torch.uint8, device=dev)
+    lib.mla_index_topk(idx, g.bt, g.attended, qi, k, pos_dev, cnt_dev, ws)
+    o, lse = _topk_inplace(lib, wl, g, pos_dev, cnt_dev)
+    _sparse_decode(lib, wl, k, g, cnt_dev, pos_dev)
+    assert _same_bits(o, g.o_lat) and _same_bits(lse, g.lse)
+
