@@ -1,8 +1,8 @@
 // Optional device-side check of the paging inputs (enabled per call by MLA_DEBUG_CHECKS=1): every
 // block-table entry that a call will dereference must name a page in [0, num_pages), every length
 // must fit the table row (decode), every append position must fall inside it (append), every kept
-// count must be at most k and every kept position must fall inside the table row (top-k decode).  The check
-// reads only entries inside the table's [batch][max_blocks] extent, so a bad table is reported
+// count must be at most k and every kept position must fall inside the table row (top-k decode).
+// The check reads only entries inside the table's [batch][max_blocks] extent, so a bad table is reported
 // without touching the cache.  It synchronises the stream to read its verdict, which is why it is
 // a debug mode and not part of the asynchronous path.
 #include "mla_device.h"

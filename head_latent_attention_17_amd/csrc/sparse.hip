@@ -15,14 +15,15 @@
 //             position order), and each chunk writes its kept positions, in increasing order.
 //   gather    copies the kept rows into compact pages (sequence b owns pages b P .. b P + P - 1,
 //             P = ceil(k / 64)) and writes their block table, so that mla_decode runs over them
-//             unchanged.
+//             unchanged.  mla_decode_topk reads the same rows in place instead (the decode
+//             kernel's list mode), with the same result.
 #include "mla_device.h"
 
 namespace mla {
 namespace {
 
 constexpr int kIndexDim = 128;
-constexpr int kChunk = 1024;          // positions per workgroup in the scoring and selection passes
+constexpr int kChunk = 1024;          // positions per workgroup in the selection passes (and scoring)
 constexpr int kBins1 = 4096;          // key >> 11: keys are score + 2^21, in [0, 2^22]
 constexpr int kBins2 = 2048;          // key & 2047
 
@@ -47,16 +48,20 @@ __global__ __launch_bounds__(256) void topk_clear_kernel(TopkWs w) {
   for (int i = threadIdx.x; i < kBins2; i += 256) w.hist2[(size_t)b * kBins2 + i] = 0;
 }
 
-// Scores of chunk blockIdx.x of sequence b (8 lanes per token, 32 tokens per step), plus the
-// histogram of their high key bits, gathered in LDS and added to the sequence's histogram.
+// Scores of the CH-token chunk blockIdx.x of sequence b (8 lanes per token, 32 tokens per step),
+// plus the histogram of their high key bits, gathered in LDS and added to the sequence's histogram.
+// CH (a multiple of 256, at most the selection chunk) is smaller when the batch has few chunks, so
+// that the grid still fills the compute units.
+template <int CH>
 __global__ __launch_bounds__(256) void index_score_kernel(const int8_t* __restrict__ index_cache,
                                                           const int32_t* __restrict__ block_table, int max_blocks,
                                                           const int32_t* __restrict__ seq_lens,
                                                           const int8_t* __restrict__ q_index, TopkWs w) {
+  static_assert(CH % 256 == 0 && CH <= kChunk, "whole rounds of eight 32-token steps");
   __shared__ int hist[kBins1];
   const int b = blockIdx.y;
   const int len = seq_lens[b];
-  const int t0 = blockIdx.x * kChunk;
+  const int t0 = blockIdx.x * CH;
   if (t0 >= len) return;
   for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0;
   __syncthreads();
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(const int8_t* __restri
   const int4 q = *reinterpret_cast<const int4*>(q_index + (size_t)b * kIndexDim + 16 * part);
   int32_t* __restrict__ scores = w.scores + (size_t)b * w.stride;
   // eight steps of 32 tokens at a time: all their loads are issued before any score is stored
-  for (int s0 = 0; s0 < kChunk / 32; s0 += 8) {
+  for (int s0 = 0; s0 < CH / 32; s0 += 8) {
     int4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -309,8 +314,17 @@ hipError_t launch_index_topk(const int8_t* index_cache, const int32_t* block_tab
   const TopkWs w = topk_ws(workspace, batch, max_blocks);
   const dim3 chunks(w.nchunks, batch);
   hipLaunchKernelGGL(topk_clear_kernel, dim3(batch), dim3(256), 0, s, w);
-  hipLaunchKernelGGL(index_score_kernel, chunks, dim3(256), 0, s, index_cache, block_table, max_blocks, seq_lens,
-                     q_index, w);
+  // Scoring chunks: 1,024 tokens, or 256 while that grid would hold fewer than two workgroups per
+  // compute unit (32 x 4,096 tokens: 12.0 -> 7.6 us).  Halving the chunks of a 516-workgroup grid
+  // (4 x 131,072 tokens) made scoring slower (20.1 -> 22.2 us): more workgroups flush their
+  // histograms into the same few hot bins.
+  if ((long long)w.nchunks * batch >= 2 * kNumCUs) {
+    hipLaunchKernelGGL(index_score_kernel<kChunk>, chunks, dim3(256), 0, s, index_cache, block_table, max_blocks,
+                       seq_lens, q_index, w);
+  } else {
+    hipLaunchKernelGGL(index_score_kernel<kChunk / 4>, dim3(4 * w.nchunks, batch), dim3(256), 0, s, index_cache,
+                       block_table, max_blocks, seq_lens, q_index, w);
+  }
   hipLaunchKernelGGL(topk_hist2_kernel, chunks, dim3(256), 0, s, seq_lens, k, w);
   hipLaunchKernelGGL(topk_count_kernel, chunks, dim3(256), 0, s, seq_lens, w);
   hipLaunchKernelGGL(topk_write_kernel, chunks, dim3(kChunk), 0, s, seq_lens, k, w, positions, counts);

@@ -51,6 +51,19 @@ def test_topk_matches_oracle(lib, k):
     _check_positions(wl, idx.cpu().numpy(), qi.cpu().numpy(), k, pos, cnt)
 
 
+def test_topk_many_chunks(lib):
+    """64 sequences of about 16,000 tokens: 1,024 selection chunks in all, so scoring runs with its
+    full 1,024-token chunks (the smaller workloads above score in 256-token chunks; the full-size
+    test below in 1,024-token chunks over 516 workgroups)."""
+    k = 300
+    wl = synth.make_custom([16384 - 7 * i for i in range(64)], heads=16, seed=145)
+    say("index top-k, 64 x ~16k tokens", k)
+    idx = synth.index_cache(wl, 0, device="cuda")
+    qi = synth.index_queries(wl, 0, device="cuda")
+    pos, cnt = _topk(lib, wl, idx, qi, k)
+    _check_positions(wl, idx.cpu().numpy(), qi.cpu().numpy(), k, pos, cnt)
+
+
 @pytest.mark.parametrize("levels", [1, 3])
 def test_topk_ties(lib, levels):
     """Index vectors with entries in {0} or {-1, 0, 1}: all scores equal, or few distinct values, so
