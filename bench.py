@@ -10,7 +10,9 @@ rotate through independent input sets.
 Prints one JSON line.  `value` is latent-cache GB/s over the whole step (tokens x 1,152 B / step
 time), from K steps timed between two synchronisations with nothing else on the stream.
 `roofline` reports the dominant call, mla_decode, timed with HIP events on the launch stream in a
-second pass of the same K steps.
+second pass of the same K steps (mean and median), against the datasheet peaks and against what
+this GPU measures on plain library work (a device copy, a bf16 matrix product); for a
+cache that fits in the Infinity Cache also warm, labelled.
 `sparse_topk` times attention over each sequence's 2,048 best tokens of a cheap int8 index (scores and
 top-k, then the decode over the kept rows read in place; beside it the form that first gathers them
 into compact pages) against the dense decode call.
@@ -39,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode: latent-cache GB/s, TFLOP/s, tokens/s; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MALL_BYTES = 256 << 20       # MI355X Infinity Cache
 MFMA_BF16_PEAK_TF = 2500.0   # MI355X dense bf16 MFMA
 ROW_BYTES = 1152
 ROW_ELEMS = 576
@@ -295,6 +298,42 @@ def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_
                             "speedup_vs_dense": round(dense_ms / ms_gather_path, 3)}}
 
 
+def measured_peaks(dev):
+    """What this GPU reaches on plain library work, as the second reference the roofline fractions are
+    quoted against: a 2 GiB device copy (bytes read + written; torch's float32 sum over the same
+    array reads at only about 4 TB/s, so it is no measure of the peak) and an 8,192-cube bf16 matrix
+    product (torch / hipBLASLt).  Each timed with HIP events, best of five after two untimed runs."""
+    import torch
+
+    def best(fn, reps=5):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+
+    n = 1 << 29                                   # 2 GiB of float32
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    copy_gbs = 2 * 4 * n / best(lambda: y.copy_(x)) / 1e9
+    del x, y
+    m = 8192
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(m, m, device=dev, generator=g).to(torch.bfloat16).contiguous()
+    b = torch.randn(m, m, device=dev, generator=g).to(torch.bfloat16).contiguous()
+    tf = 2 * m ** 3 / best(lambda: torch.matmul(a, b)) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": round(copy_gbs, 1), "mfma_bf16_tflops": round(tf, 1),
+            "how": "2 GiB device copy (read + write bytes); 8192^3 bf16 matmul; best of 5"}
+
+
 def cpu_baseline(wl, seconds: float):
     """The oracle (decompressed form, float64) on whole sequences of the same workload, in order,
     until `seconds` of work are done.  Rate = latent-cache bytes of the finished sequences per
@@ -325,9 +364,12 @@ def cpu_baseline(wl, seconds: float):
         seqs += 1
         if busy >= seconds:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in pools] or [1])
+    blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in pools
+                             if i.get("user_api") == "blas"})) or "none found"
     gbs = done_tokens * ROW_BYTES / busy / 1e9
-    return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle", "blas": blas,
             "sample": f"decode_reference (decompressed, float64): {seqs} of {wl.batch} sequences "
                       f"({done_tokens} attended tokens, all {wl.heads} heads, append + gather included) "
                       f"in {busy:.1f} s of oracle time; host has {len(os.sched_getaffinity(0))} usable cores"}
@@ -490,7 +532,28 @@ def main():
     for i in range(args.steps):
         step(i, timed=True)
     torch.cuda.synchronize()
-    dec_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    dec_times = sorted(a.elapsed_time(b) for a, b in ev)
+    dec_ms = sum(dec_times) / len(dec_times)
+    dec_median = dec_times[len(dec_times) // 2]
+    # Warm numbers, labelled: when the cache fits in the 256 MB Infinity Cache, the same input set
+    # every call (the steps above rotate sets so that each call reads HBM).
+    warm = None
+    if cache_bytes < MALL_BYTES and layers == 1:
+        d = inst[0]
+        for _ in range(3):
+            lib.mla_decode(q_abs, d["cache"], bt, att, wl.scale, o_lat, lse, ws, args.splits)
+        wev = []
+        for _ in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            lib.mla_decode(q_abs, d["cache"], bt, att, wl.scale, o_lat, lse, ws, args.splits)
+            b.record(stream)
+            wev.append((a, b))
+        torch.cuda.synchronize()
+        wms = sum(a.elapsed_time(b) for a, b in wev) / len(wev)
+        warm = {"label": "warm: one input set, cache resident in the Infinity Cache",
+                "ms_per_launch": round(wms, 5), "achieved": round(cache_bytes / (wms * 1e-3) / 1e9, 2)}
+    peaks = measured_peaks(dev)
 
     decode_flops = N * 2 * H * (D_C + D_R + D_C)
     proj_flops = 2 * 2 * B * H * D_NOPE * D_C
@@ -517,9 +580,15 @@ def main():
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_call"],
                      "ms_per_launch": round(dec_ms, 5),
+                     "ms_per_launch_median": round(dec_median, 5),
                      "mfma_tflops": round(dec_tf, 2),
-                     "mfma_frac": round(dec_tf / MFMA_BF16_PEAK_TF, 4)},
+                     "mfma_frac": round(dec_tf / MFMA_BF16_PEAK_TF, 4),
+                     "measured_peaks": peaks,
+                     "frac_of_measured_copy": round(dec_gbs / peaks["hbm_copy_gbs"], 4),
+                     "mfma_frac_of_measured": round(dec_tf / peaks["mfma_bf16_tflops"], 4)},
     }
+    if warm is not None:
+        line["roofline"]["warm"] = warm
     if wl.append:  # the table has a slot at each sequence's next position only when the workload appends
         line["producer"] = producer_timing(lib, synth, wl, dev, inst[0]["cache"], bt, lens, args.steps)
     sp = sparse_timing(lib, synth, wl, dev, q_abs, bt, att, inst[0]["cache"], args.steps, dec_ms)
