@@ -108,6 +108,27 @@ def test_out_proj_matches_oracle(lib, f32):
     assert e <= _tol(f32)
 
 
+@pytest.mark.parametrize("heads,batch", [(16, 3), (128, 32), (128, 65), (16, 130), (128, 130)])
+def test_projections_batch_blocks(lib, heads, batch):
+    """Absorption and out-projection (bf16) against the oracle with 16 and 128 heads: batch 3 and 32
+    (one 32-row block), 65 (three blocks in one pass of the four-block kernel) and 130 (five
+    blocks, two passes, the last with two rows)."""
+    wl = synth.make_custom([3] * batch, heads=heads, seed=62 + batch)
+    say("projections", heads, batch)
+    g = Gpu(wl)
+    lib.mla_absorb_q(g.q, g.w_uk, g.q_abs)
+    o_in = g.q_lat_in[..., :synth.D_C].contiguous()
+    lib.mla_out_proj(o_in, g.w_uv, g.out)
+    torch.cuda.synchronize()
+    q = synth.to_numpy_u16(synth.queries(wl))
+    w_uk, w_uv = (synth.to_numpy_u16(w) for w in synth.weights(wl))
+    e_q = rel_err(to_host_f64(g.q_abs), O.absorb_batch(q, w_uk))
+    e_o = rel_err(to_host_f64(g.out), O.out_proj_batch(synth.to_numpy_u16(synth.latent_queries(wl))[..., :synth.D_C],
+                                                       w_uv))
+    say(f"  q_abs {e_q:.3e} out {e_o:.3e}")
+    assert e_q <= BF16_TOL and e_o <= BF16_TOL
+
+
 @pytest.mark.parametrize("heads", [16, 128])
 def test_empty_sequences(lib, heads):
     """Empty sequences give zeros and lse = -inf.  With 8 splits of 3 pages most work units hold no
