@@ -292,6 +292,13 @@ mla_status mla_gather_rows(const void* kv_cache, int num_pages, int page_size, c
   if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1 || k < 1) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!kv_cache || !block_table || !positions || !counts || !out_cache || !out_block_table) return MLA_ERR_NULL;
+  if (debug_checks_enabled()) {
+    bool bad = false;
+    if (check_positions(block_table, max_blocks_per_seq, positions, counts, batch, k, num_pages, stream, &bad) !=
+        hipSuccess)
+      return MLA_ERR_HIP;
+    if (bad) return MLA_ERR_BLOCK_TABLE;
+  }
   hipError_t e = launch_gather_rows(kv_cache, block_table, max_blocks_per_seq, positions, counts, batch, k, out_cache,
                                     out_block_table, stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;

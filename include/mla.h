@@ -37,11 +37,12 @@
  *   - Every entry point validates its arguments on the host before launching anything and returns a
  *     negative mla_status on error, without touching any buffer.  Launch failures are reported as
  *     MLA_ERR_HIP.  Nothing is thrown across the ABI.
- *   - Device-side contents (block-table entries, lengths) are trusted: an entry outside
- *     [0, num_pages) or a length above max_blocks_per_seq * 64 is undefined behaviour.  With the
- *     environment variable MLA_DEBUG_CHECKS=1 (read at every call), mla_cache_append and mla_decode
- *     first check on the device every entry they would use, synchronise the stream to read the
- *     verdict, and return MLA_ERR_BLOCK_TABLE, launching nothing else, if one is out of range.
+ *   - Device-side contents (block-table entries, lengths, positions, kept counts) are trusted: an
+ *     entry outside [0, num_pages) or a length above max_blocks_per_seq * 64 is undefined
+ *     behaviour.  With the environment variable MLA_DEBUG_CHECKS=1 (read at every call), every
+ *     call that reads the block table (the appends, the decodes, mla_index_topk, mla_gather_rows)
+ *     first checks on the device every entry it would use, synchronises the stream to read the
+ *     verdict, and returns MLA_ERR_BLOCK_TABLE, launching nothing else, if one is out of range.
  *   - Calls that share a workspace must be ordered on one stream.
  */
 #ifndef MLA_H
@@ -235,7 +236,9 @@ mla_status mla_out_proj_hidden(const void* out, const void* w_o, void* hidden, i
  * and out_block_table [batch][P] gets b * P + j; mla_decode over (out_cache, out_block_table,
  * counts) is then the attention over the kept tokens.
  * Errors: MLA_ERR_UNSUPPORTED unless page_size is 64; MLA_ERR_SHAPE for k < 1 or bad sizes;
- * MLA_ERR_NULL, MLA_ERR_WORKSPACE; with MLA_DEBUG_CHECKS=1, MLA_ERR_BLOCK_TABLE as mla_decode.
+ * MLA_ERR_NULL, MLA_ERR_WORKSPACE (mla_index_topk); with MLA_DEBUG_CHECKS=1, MLA_ERR_BLOCK_TABLE:
+ * for mla_index_topk as mla_decode, for mla_gather_rows a count above k, a position outside the
+ * table row or a table entry outside [0, num_pages).
  */
 #define MLA_INDEX_DIM 128
 size_t mla_index_topk_workspace_size(int batch, int max_blocks_per_seq);

@@ -244,7 +244,8 @@ def test_decode_topk_arbitrary_lists(lib):
 
 def test_decode_topk_debug_checks(lib, monkeypatch):
     """MLA_DEBUG_CHECKS=1: valid lists give the unchecked result bit for bit; a count above k or a
-    position outside the table row is reported as MLA_ERR_BLOCK_TABLE before any decode launch."""
+    position outside the table row is reported as MLA_ERR_BLOCK_TABLE before any decode (or gather)
+    launch."""
     k = 64
     wl = synth.make_custom([100, 300], heads=128, seed=210)
     say("in-place top-k decode, debug checks")
@@ -267,6 +268,16 @@ def test_decode_topk_debug_checks(lib, monkeypatch):
     with pytest.raises(lib.MLAError) as e:
         _topk_inplace(lib, wl, g, torch.from_numpy(bad_pos).cuda(), cnt_dev)
     assert e.value.status == -6
+    # the gather reads the same lists and is checked the same way
+    pk = -(-k // 64)
+    out_cache = torch.empty((wl.batch * pk, 64, 576), dtype=torch.bfloat16, device="cuda")
+    out_bt = torch.full((wl.batch, pk), -1, dtype=torch.int32, device="cuda")
+    lib.mla_gather_rows(g.cache, g.bt, pos_dev, cnt_dev, out_cache, out_bt)
+    torch.cuda.synchronize()
+    for p_bad, c_bad in ((torch.from_numpy(bad_pos).cuda(), cnt_dev), (pos_dev, bad_cnt)):
+        with pytest.raises(lib.MLAError) as e:
+            lib.mla_gather_rows(g.cache, g.bt, p_bad, c_bad, out_cache, out_bt)
+        assert e.value.status == -6
 
 
 def test_decode_topk_full_size(lib):
