@@ -26,8 +26,6 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   __shared__ float q_s[kHG][kQStride];
   __shared__ uint32_t kv_s[kTile][kRowDw];
   __shared__ float s_s[kHG][kTile + 1];
-  __shared__ float alpha_s[kHG];
-  __shared__ float stat_s[kHG][2];
 
   const int tid = threadIdx.x;
   const int w = blockIdx.x;
@@ -42,34 +40,81 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   while (walk.next(seg)) {
     const int b = seg.b;
     __syncthreads();
-    for (int i = tid; i < kHG * kRow; i += 256) {
-      const int h = i / kRow, k = i % kRow;
-      q_s[h][k] = Elem<QT>::load(q_abs, ((size_t)b * p.heads + h0 + h) * kRow + k);
+    {
+      // The heads' query rows as groups of 8 numbers (16 bytes in bf16, 32 in fp32), every load in
+      // flight before the first store.
+      constexpr int kGroups = kHG * kRow / 8;
+      constexpr int kIters = (kGroups + 255) / 256;
+      float qv[kIters][8];
+#pragma unroll
+      for (int u = 0; u < kIters; ++u) {
+        const int i = tid + 256 * u;
+        if (i < kGroups) {
+          const QT* src = q_abs + ((size_t)b * p.heads + h0 + i / (kRow / 8)) * kRow + 8 * (i % (kRow / 8));
+          if constexpr (sizeof(QT) == 2) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              qv[u][2 * j] = bf16_lo(w4[j]);
+              qv[u][2 * j + 1] = bf16_hi(w4[j]);
+            }
+          } else {
+            const float4 a = *reinterpret_cast<const float4*>(src);
+            const float4 c = *reinterpret_cast<const float4*>(src + 4);
+            qv[u][0] = a.x; qv[u][1] = a.y; qv[u][2] = a.z; qv[u][3] = a.w;
+            qv[u][4] = c.x; qv[u][5] = c.y; qv[u][6] = c.z; qv[u][7] = c.w;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kIters; ++u) {
+        const int i = tid + 256 * u;
+        if (i < kGroups) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) q_s[i / (kRow / 8)][8 * (i % (kRow / 8)) + j] = qv[u][j];
+        }
+      }
     }
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;  // meaningful in threads tid < kHG (head tid)
+    float m_run = -INFINITY, l_run = 0.f;  // the same in the 16 lanes of a head
 
     const int t_begin = seg.page0 * kPage;
     const int t_end = min(seg.page1 * kPage, seg.len);
     const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
-    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+    // A tile is 32 x 72 pieces of 16 bytes, nine per thread; the next tile's pieces are loaded into
+    // registers while the current one is computed.  Rows past the end re-read the last valid token
+    // (finite, masked below), so no slot beyond the sequence and no unused block-table entry is
+    // ever touched.
+    constexpr int kPieces = kTile * (kRow / 8) / 256;
+    uint4 pre[kPieces];
+    auto load_tile = [&](int t0) {
       const int nt = min(kTile, t_end - t0);
-      __syncthreads();
-      // Stage the tile.  Rows past the end re-read the last valid token (finite, masked below),
-      // so no slot beyond the sequence and no unused block-table entry is ever touched.
-      for (int i = tid; i < kTile * (kRow / 8); i += 256) {
+#pragma unroll
+      for (int u = 0; u < kPieces; ++u) {
+        const int i = tid + 256 * u;
         const int r = i / (kRow / 8), c = i % (kRow / 8);
         const int t = t0 + min(r, nt - 1);
         const int page = bt[t / kPage];
-        const uint4 v = reinterpret_cast<const uint4*>(p.cache + ((size_t)page * kPage + (t % kPage)) * kRow)[c];
-        uint32_t* dst = &kv_s[r][c * 4];
-        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+        pre[u] = reinterpret_cast<const uint4*>(p.cache + ((size_t)page * kPage + (t % kPage)) * kRow)[c];
+      }
+    };
+    if (t_begin < t_end) load_tile(t_begin);
+    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+      const int nt = min(kTile, t_end - t0);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kPieces; ++u) {
+        const int i = tid + 256 * u;
+        uint32_t* dst = &kv_s[i / (kRow / 8)][(i % (kRow / 8)) * 4];
+        dst[0] = pre[u].x; dst[1] = pre[u].y; dst[2] = pre[u].z; dst[3] = pre[u].w;
       }
       __syncthreads();
+      if (t0 + kTile < t_end) load_tile(t0 + kTile);
+      float s0 = 0.f, s1 = 0.f;
       {
-        float s0 = 0.f, s1 = 0.f;
         const uint32_t* r0 = kv_s[j16];
         const uint32_t* r1 = kv_s[j16 + 16];
         const float* qh = q_s[hh];
@@ -82,27 +127,25 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
           s1 = fmaf(qa, bf16_lo(c), s1);
           s1 = fmaf(qb, bf16_hi(c), s1);
         }
-        s_s[hh][j16] = (j16 < nt) ? s0 * p.scale_log2 : -INFINITY;
-        s_s[hh][j16 + 16] = (j16 + 16 < nt) ? s1 * p.scale_log2 : -INFINITY;
+        s0 = (j16 < nt) ? s0 * p.scale_log2 : -INFINITY;
+        s1 = (j16 + 16 < nt) ? s1 * p.scale_log2 : -INFINITY;
       }
+      // Online softmax of the head's 32 scores across its 16 lanes (two scores each); token 0 of a
+      // tile is always valid, so the tile maximum is finite.
+      float mx = fmaxf(s0, s1);
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+      const float e0 = exp2f(s0 - m_new), e1 = exp2f(s1 - m_new);
+      float sum = e0 + e1;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+      l_run = l_run * alpha + sum;
+      m_run = m_new;
+      s_s[hh][j16] = e0;
+      s_s[hh][j16 + 16] = e1;
       __syncthreads();
-      if (tid < kHG) {
-        float mx = -INFINITY;
-        for (int t = 0; t < kTile; ++t) mx = fmaxf(mx, s_s[tid][t]);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
-        float sum = 0.f;
-        for (int t = 0; t < kTile; ++t) {
-          const float e = exp2f(s_s[tid][t] - m_new);
-          s_s[tid][t] = e;
-          sum += e;
-        }
-        l_run = l_run * alpha + sum;
-        m_run = m_new;
-        alpha_s[tid] = alpha;
-      }
-      __syncthreads();
-      const float alpha = alpha_s[hh];
 #pragma unroll
       for (int i = 0; i < 32; ++i) acc[i] *= alpha;
       for (int t = 0; t < kTile; ++t) {
@@ -116,18 +159,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
         }
       }
     }
-    if (tid < kHG) {
-      stat_s[tid][0] = m_run;
-      stat_s[tid][1] = l_run;
-    }
-    __syncthreads();
     // Un-normalised partial sum plus (reference max, softmax sum); the merge kernel finishes it.
     const size_t part = ((size_t)w + b) * p.heads + h0 + hh;
     float* o = p.ws_o + part * kDc;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       *reinterpret_cast<float2*>(o + 32 * j + 2 * j16) = make_float2(acc[2 * j], acc[2 * j + 1]);
-    if (j16 == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(stat_s[hh][0], stat_s[hh][1]);
+    if (j16 == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_run, l_run);
   }
 }
 

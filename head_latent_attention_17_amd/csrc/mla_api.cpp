@@ -51,7 +51,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: invalid or inconsistent size";
     case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown dtype";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
-    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: page_size must be 64, heads in {16,32,64,128} (64 or 128 and bf16 for the ~6-bit cache)";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: page_size must be 64, heads in {16,32,64,128} (64 or 128 and bf16 for the ~6-bit cache, 32 to 128 for mla_decode_topk)";
     case MLA_ERR_BLOCK_TABLE: return "MLA_ERR_BLOCK_TABLE: block table entry out of range";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch failed";
     default: return "unknown mla_status";
