@@ -18,7 +18,7 @@ namespace {
 
 constexpr int kTile = 32;             // tokens per LDS tile
 constexpr int kRowDw = kRow / 2 + 1;  // 289 dwords per LDS row: consecutive rows start on different banks
-constexpr int kHG = 16;               // heads per workgroup
+constexpr int kHG = 8;                // heads per workgroup (32 lanes each)
 constexpr int kQStride = kRow + 2;    // fp32 query rows, padded
 
 template <typename QT, typename OT>
@@ -30,8 +30,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int w = blockIdx.x;
   const int h0 = blockIdx.y * kHG;
-  const int hh = tid >> 4;     // head within the group
-  const int j16 = tid & 15;    // token lane for scores, dword lane for the weighted sum
+  const int hh = tid >> 5;     // head within the group
+  const int j32 = tid & 31;    // token of the tile for its score, dword lane for the weighted sum
   const QT* q_abs = static_cast<const QT*>(p.q_abs);
 
   SegmentWalker walk;
@@ -76,10 +76,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
         }
       }
     }
-    float acc[32];
+    float acc[16];  // latent dims 64 j + 2 j32 + {0, 1}, j < 8
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;  // the same in the 16 lanes of a head
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;  // the same in the 32 lanes of a head
 
     const int t_begin = seg.page0 * kPage;
     const int t_end = min(seg.page1 * kPage, seg.len);
@@ -113,47 +113,41 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
       }
       __syncthreads();
       if (t0 + kTile < t_end) load_tile(t0 + kTile);
-      float s0 = 0.f, s1 = 0.f;
+      float s0 = 0.f, s1 = 0.f;  // even and odd dims of the score of token j32
       {
-        const uint32_t* r0 = kv_s[j16];
-        const uint32_t* r1 = kv_s[j16 + 16];
+        const uint32_t* r0 = kv_s[j32];
         const float* qh = q_s[hh];
 #pragma unroll 8
         for (int k2 = 0; k2 < kRow / 2; ++k2) {
-          const float qa = qh[2 * k2], qb = qh[2 * k2 + 1];
-          const uint32_t a = r0[k2], c = r1[k2];
-          s0 = fmaf(qa, bf16_lo(a), s0);
-          s0 = fmaf(qb, bf16_hi(a), s0);
-          s1 = fmaf(qa, bf16_lo(c), s1);
-          s1 = fmaf(qb, bf16_hi(c), s1);
+          const uint32_t a = r0[k2];
+          s0 = fmaf(qh[2 * k2], bf16_lo(a), s0);
+          s1 = fmaf(qh[2 * k2 + 1], bf16_hi(a), s1);
         }
-        s0 = (j16 < nt) ? s0 * p.scale_log2 : -INFINITY;
-        s1 = (j16 + 16 < nt) ? s1 * p.scale_log2 : -INFINITY;
+        s0 = (j32 < nt) ? (s0 + s1) * p.scale_log2 : -INFINITY;
       }
-      // Online softmax of the head's 32 scores across its 16 lanes (two scores each); token 0 of a
-      // tile is always valid, so the tile maximum is finite.
-      float mx = fmaxf(s0, s1);
+      // Online softmax of the head's 32 scores across its 32 lanes; token 0 of a tile is always
+      // valid, so the tile maximum is finite.
+      float mx = s0;
 #pragma unroll
-      for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+      for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);
-      const float e0 = exp2f(s0 - m_new), e1 = exp2f(s1 - m_new);
-      float sum = e0 + e1;
+      const float e0 = exp2f(s0 - m_new);
+      float sum = e0;
 #pragma unroll
-      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+      for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 32);
       l_run = l_run * alpha + sum;
       m_run = m_new;
-      s_s[hh][j16] = e0;
-      s_s[hh][j16 + 16] = e1;
+      s_s[hh][j32] = e0;
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+      for (int i = 0; i < 16; ++i) acc[i] *= alpha;
       for (int t = 0; t < kTile; ++t) {
         const float pt = s_s[hh][t];
         const uint32_t* rv = kv_s[t];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {  // latent dims 32 j + 2 j16 + {0, 1}
-          const uint32_t v = rv[j * 16 + j16];
+        for (int j = 0; j < 8; ++j) {  // latent dims 64 j + 2 j32 + {0, 1}
+          const uint32_t v = rv[j * 32 + j32];
           acc[2 * j] = fmaf(pt, bf16_lo(v), acc[2 * j]);
           acc[2 * j + 1] = fmaf(pt, bf16_hi(v), acc[2 * j + 1]);
         }
@@ -163,9 +157,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
     const size_t part = ((size_t)w + b) * p.heads + h0 + hh;
     float* o = p.ws_o + part * kDc;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      *reinterpret_cast<float2*>(o + 32 * j + 2 * j16) = make_float2(acc[2 * j], acc[2 * j + 1]);
-    if (j16 == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_run, l_run);
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<float2*>(o + 64 * j + 2 * j32) = make_float2(acc[2 * j], acc[2 * j + 1]);
+    if (j32 == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_run, l_run);
   }
 }
 
