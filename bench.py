@@ -1,29 +1,35 @@
-"""Benchmark: one MLA decode step over a paged latent cache on one MI355X.
+"""Benchmark: MLA decode steps over a paged latent cache on one MI355X.
 
-A step is the whole path for one batch: cache append (one new row per sequence), query absorption
-through W_UK, latent decode attention (with its split merge) and the W_UV out-projection.  Inputs are
-seeded synthetic data resident in HBM before timing starts.  Default workload: 32 sequences x 4,096
-cached tokens, each appending its new token's row (so 4,097 are attended), 128 heads, 64-token pages
-with a shuffled block table.  The 151 MB cache fits in the 256 MB Infinity Cache, so the steps
-rotate through independent input sets.
+A step is the whole path for one batch and every layer: query absorption through W_UK, latent
+decode attention (with its split merge) and the W_UV out-projection, plus the cache append of one
+new row per sequence in the one-layer workloads.  Inputs are seeded synthetic data resident in HBM
+before timing starts.
 
-Prints one JSON line.  `value` is latent-cache GB/s over the whole step (tokens x 1,152 B / step
-time), from K steps timed between two synchronisations with nothing else on the stream.
+Default workload (the headline line): the full 60-layer decode step, 64 sequences with cached
+lengths uniform in [4,096, 8,192], 128 heads, 64-token pages with a shuffled block table, each layer
+with its own cache, W_UK, W_UV and query (27 GB of cache per step).
+
+Prints one JSON line.  `value` is latent-cache GB/s over the whole step (layers x tokens x 1,152 B /
+step time), from K steps timed between two synchronisations with nothing else on the stream.
 `roofline` reports the dominant call, mla_decode, timed with HIP events on the launch stream in a
-second pass of the same K steps (mean and median), against the datasheet peaks and against what
-this GPU measures on plain library work (a device copy, a bf16 matrix product); for a
-cache that fits in the Infinity Cache also warm, labelled.
-`sparse_topk` times attention over each sequence's 2,048 best tokens of a cheap int8 index (scores and
-top-k, then the decode over the kept rows read in place; beside it the form that first gathers them
-into compact pages) against the dense decode call.
-`out_proj_hidden` times the projection of the step's per-head output to the hidden width through W^O.
-`producer` (workloads that append) times mla_cache_append_hidden, the producer side of the cache,
-graph-replayed over 48 weight copies.  `fp6` times mla_decode_fp6 over the ~6-bit form of the same
-cache (FP6 codes and a power-of-two scale per row, 436 bytes per token).
-`cpu_baseline` times the CPU oracle (decompressed form, float64) on a bounded sample: whole
-sequences (gather + every head), in order, until about --cpu-seconds of work is done.
+second pass of the same K steps (mean and median per layer call), against the datasheet peaks and
+against what this GPU measures on plain library work (a device copy, a bf16 matrix product).
+`calls_per_layer` gives the other calls of a layer the same way.
 
-    python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+Blocks `c3`, `c2`, `c4`, `c1` time the other workloads the same way (a whole step, then each call):
+4 x 131,072 tokens (the long-context decode), 32 x 4,096 (the batched decode whose matrix-core
+fraction is the one to read), 128 ragged sequences and the 16-head single sequence.  A cache that
+fits the 256 MB Infinity Cache is rotated through four independent input sets and also timed warm,
+labelled.  The further calls are measured on the long-context and batched workloads:
+`sparse_topk` (attention over each sequence's 2,048 best tokens of a cheap int8 index, read in
+place, beside the form that first gathers them), `fp6` (mla_decode_fp6 over the ~6-bit form of the
+same cache), and on the batched one `out_proj_hidden` (the projection to the hidden width through
+W^O) and `producer` (mla_cache_append_hidden, graph-replayed over 48 weight copies).
+`cpu_baseline` times the CPU oracle (decompressed form, float64) on a bounded sample of the headline
+workload: whole sequences of its first layer (gather + every head), in order, until about
+--cpu-seconds of work is done.
+
+    python bench.py [--steps K] [--warmup W] [--config 1..5] [--main-only] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -55,7 +61,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--main-only", action="store_true", help="time only the --config workload")
     ap.add_argument("--sets", type=int, default=0, help="independent input sets (0 = auto)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -374,7 +381,8 @@ def cpu_baseline(wl, seconds: float):
     gbs = done_tokens * ROW_BYTES / busy / 1e9
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle", "blas": blas,
             "sample": f"decode_reference (decompressed, float64): {seqs} of {wl.batch} sequences "
-                      f"({done_tokens} attended tokens, all {wl.heads} heads, append + gather included) "
+                      f"({done_tokens} attended tokens, all {wl.heads} heads, "
+                      f"{'append + ' if wl.append else ''}gather included{', first layer' if wl.layers > 1 else ''}) "
                       f"in {busy:.1f} s of oracle time; host has {len(os.sched_getaffinity(0))} usable cores"}
 
 
@@ -424,7 +432,9 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str):
 
 def bench_workload(config: int):
     """The timed workload: the numbered configuration, with one appended row per sequence when the
-    configuration itself has none (a decode step appends the new token before attending)."""
+    configuration itself has none and is one layer (a decode step appends the new token before
+    attending).  The 60-layer workload is timed as it is stated: absorb, decode and out-projection
+    per layer, no append."""
     import synth
 
     wl = synth.make_config(config)
@@ -432,6 +442,177 @@ def bench_workload(config: int):
         return wl
     return synth.make_custom(wl.lens, wl.heads, wl.seed, shuffle=config != 1, append=True,
                              name=wl.name + "+append")
+
+
+class Resident:
+    """One workload's inputs resident in HBM: per-layer (or per rotation set) cache, query and weights,
+    the shared block table and lengths, and the step's outputs."""
+
+    def __init__(self, lib, synth, wl, dev, sets: int, splits: int):
+        import torch
+        self.wl, self.splits = wl, splits
+        B, H = wl.batch, wl.heads
+        self.layers = wl.layers
+        self.cache_bytes = wl.tokens * ROW_BYTES
+        self.sets = sets or (4 if self.cache_bytes < 256e6 else 1)
+        n_inst = max(self.layers, self.sets)
+        self.bt = torch.as_tensor(wl.block_table, device=dev)
+        self.lens = torch.as_tensor(wl.lens, device=dev)
+        self.att = torch.as_tensor(wl.attended_lens.astype(np.int32), device=dev)
+        self.inst = []
+        for i in range(n_inst):
+            # config seeds give each layer its own draws; extra rotation sets reuse the layer streams
+            # with a distinct layer index so their bytes differ
+            cache = synth.cache_pages(wl, i, device=dev, chunk_pages=2048).view(torch.bfloat16)
+            q = synth.queries(wl, i, device=dev).view(torch.bfloat16)
+            w_uk, w_uv = (w.view(torch.bfloat16) for w in synth.weights(wl, i, device=dev))
+            rows = synth.new_rows(wl, i, device=dev).view(torch.bfloat16)
+            self.inst.append(dict(cache=cache, q=q, w_uk=w_uk, w_uv=w_uv, c_new=rows[:, :D_C].contiguous(),
+                                  kpe_new=rows[:, D_C:].contiguous()))
+        self.q_abs = torch.empty(B, H, D_C + D_R, dtype=torch.bfloat16, device=dev)
+        self.o_lat = torch.empty(B, H, D_C, dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty(B, H, D_V, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(lib.mla_decode_workspace_size(B, H, wl.max_blocks, splits), dtype=torch.uint8,
+                              device=dev)
+
+    def decode(self, lib, d):
+        wl = self.wl
+        lib.mla_decode(self.q_abs, d["cache"], self.bt, self.att, wl.scale, self.o_lat, self.lse, self.ws,
+                       self.splits)
+
+    def layer(self, lib, d, marks=None):
+        """One layer of the step; with `marks` (five events) each call is bracketed on the stream."""
+        wl = self.wl
+        if marks: marks[0].record()
+        if wl.append:
+            lib.mla_cache_append(d["cache"], self.bt, self.lens, d["c_new"], d["kpe_new"])
+        if marks: marks[1].record()
+        lib.mla_absorb_q(d["q"], d["w_uk"], self.q_abs)
+        if marks: marks[2].record()
+        self.decode(lib, d)
+        if marks: marks[3].record()
+        lib.mla_out_proj(self.o_lat, d["w_uv"], self.out)
+        if marks: marks[4].record()
+
+    def step(self, lib, i, marks_out=None):
+        import torch
+        ds = self.inst[:self.layers] if self.layers > 1 else [self.inst[i % self.sets]]
+        for d in ds:
+            marks = None
+            if marks_out is not None:
+                marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                marks_out.append(marks)
+            self.layer(lib, d, marks)
+
+
+def time_workload(lib, res: Resident, steps: int, warmup: int) -> dict:
+    """Whole steps between two synchronisations (nothing but the path's kernels on the stream), then
+    a second pass of the same steps with HIP events around every call of every layer, on the stream
+    the calls are launched on (torch's current stream, which the binding passes to the library)."""
+    import torch
+    wl = res.wl
+    for i in range(warmup):
+        res.step(lib, i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        res.step(lib, i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    marks = []
+    for i in range(steps):
+        res.step(lib, i, marks)
+    torch.cuda.synchronize()
+    per_call = {}
+    for k, name in enumerate(("append", "absorb", "decode", "out_proj")):
+        ts = sorted(m[k].elapsed_time(m[k + 1]) for m in marks)
+        per_call[name] = (sum(ts) / len(ts), ts[len(ts) // 2])
+    N = wl.tokens
+    dec_ms, dec_med = per_call["decode"]
+    decode_flops = N * 2 * wl.heads * (D_C + D_R + D_C)
+    dec_gbs = res.cache_bytes / (dec_ms * 1e-3) / 1e9
+    dec_tf = decode_flops / (dec_ms * 1e-3) / 1e12
+    traffic = traffic_record(wl.name)
+    calls = {"decode": {"ms_per_launch": round(dec_ms, 5), "ms_per_launch_median": round(dec_med, 5)}}
+    wbytes = wl.heads * D_NOPE * D_C * 2
+    for name in ("absorb", "out_proj"):
+        ms = per_call[name][0]
+        calls[name] = {"ms_per_launch": round(ms, 5), "weight_gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                       "weight_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if wl.append:
+        calls["append"] = {"ms_per_launch": round(per_call["append"][0], 5)}
+    out = {
+        "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "layers": res.layers,
+        "attended_tokens_per_layer": N, "input_sets": res.sets, "ms_per_step": round(ms_step, 5),
+        "step": ("append+" if wl.append else "") + "absorb+decode+out_proj",
+        "decode_call": {"kernels": "mla_decode", "bound": "hbm", "achieved": round(dec_gbs, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                        "traffic": None if traffic is None else traffic["bytes_per_call"],
+                        "ms_per_launch": round(dec_ms, 5), "ms_per_launch_median": round(dec_med, 5),
+                        "mfma_tflops": round(dec_tf, 2), "mfma_frac": round(dec_tf / MFMA_BF16_PEAK_TF, 4)},
+        "calls_per_layer": calls,
+    }
+    # Warm numbers, labelled: when the cache fits in the 256 MB Infinity Cache, the same input set
+    # every call (the steps above rotate sets so that each call reads HBM).
+    if res.cache_bytes < MALL_BYTES and res.layers == 1:
+        d = res.inst[0]
+        for _ in range(3):
+            res.decode(lib, d)
+        wev = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            res.decode(lib, d)
+            b.record()
+            wev.append((a, b))
+        torch.cuda.synchronize()
+        wms = sum(a.elapsed_time(b) for a, b in wev) / len(wev)
+        out["decode_call"]["warm"] = {"label": "warm: one input set, cache resident in the Infinity Cache",
+                                      "ms_per_launch": round(wms, 5),
+                                      "achieved": round(res.cache_bytes / (wms * 1e-3) / 1e9, 2)}
+    return out
+
+
+def side_records(lib, synth, res: Resident, dev, steps: int, which) -> dict:
+    """The further calls on one workload's inputs (layer 0): top-k attention, the ~6-bit decode, the
+    output to the hidden width and the producer side of the cache."""
+    wl = res.wl
+    d = res.inst[0]
+    dec_ms = None
+    rec = {}
+    # a fresh decode time on this workload's first input set, the baseline of the two ratios
+    import torch
+    for _ in range(3):
+        res.decode(lib, d)
+    ev = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        res.decode(lib, d)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    dec_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    lib.mla_absorb_q(d["q"], d["w_uk"], res.q_abs)
+    if "sparse_topk" in which:
+        sp = sparse_timing(lib, synth, wl, dev, res.q_abs, res.bt, res.att, d["cache"], steps, dec_ms)
+        if sp is not None:
+            rec["sparse_topk"] = sp
+    if "fp6" in which:
+        fp6 = fp6_timing(lib, synth, wl, dev, res.q_abs, res.bt, res.att, res.o_lat, res.lse, res.ws, steps,
+                         res.splits, dec_ms)
+        if fp6 is not None:
+            rec["fp6"] = fp6
+    if "out_proj_hidden" in which:
+        res.decode(lib, d)
+        lib.mla_out_proj(res.o_lat, d["w_uv"], res.out)
+        oh = out_hidden_timing(lib, synth, wl, dev, res.out, steps)
+        if oh is not None:
+            rec["out_proj_hidden"] = oh
+    if "producer" in which and wl.append:
+        rec["producer"] = producer_timing(lib, synth, wl, dev, d["cache"], res.bt, res.lens, steps)
+    return rec
 
 
 def main():
@@ -453,157 +634,79 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = bench_workload(args.config)
-    B, H = wl.batch, wl.heads
-    layers = wl.layers
-    N = wl.tokens                           # attended tokens per layer
-    cache_bytes = N * ROW_BYTES
-    sets = args.sets or (4 if cache_bytes < 256e6 else 1)
-    n_inst = max(layers, sets)              # independent input sets actually allocated
+    say = lambda *a: print("bench:", *a, file=sys.stderr, flush=True)  # noqa: E731
+    say(f"{wl.name}, {wl.tokens} tokens per layer, {wl.layers} layer(s)")
+    res = Resident(lib, synth, wl, dev, args.sets, args.splits)
 
-    bt = torch.as_tensor(wl.block_table, device=dev)
-    lens = torch.as_tensor(wl.lens, device=dev)
-    att = torch.as_tensor(wl.attended_lens.astype(np.int32), device=dev)
-    inst = []
-    for i in range(n_inst):
-        # config seeds give each layer its own draws; extra rotation sets reuse the layer streams
-        # with a distinct layer index so their bytes differ
-        layer = i
-        cache = synth.cache_pages(wl, layer, device=dev, chunk_pages=2048).view(torch.bfloat16)
-        q = synth.queries(wl, layer, device=dev).view(torch.bfloat16)
-        w_uk, w_uv = (w.view(torch.bfloat16) for w in synth.weights(wl, layer, device=dev))
-        rows = synth.new_rows(wl, layer, device=dev).view(torch.bfloat16)
-        inst.append(dict(cache=cache, q=q, w_uk=w_uk, w_uv=w_uv, c_new=rows[:, :D_C].contiguous(),
-                         kpe_new=rows[:, D_C:].contiguous()))
-    q_abs = torch.empty(B, H, D_C + D_R, dtype=torch.bfloat16, device=dev)
-    o_lat = torch.empty(B, H, D_C, dtype=torch.bfloat16, device=dev)
-    out = torch.empty(B, H, D_V, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
-    ws = torch.empty(lib.mla_decode_workspace_size(B, H, wl.max_blocks, args.splits), dtype=torch.uint8,
-                     device=dev)
-    stream = torch.cuda.current_stream()
-    ev = []
-
-    def one_layer(d, timed):
-        if wl.append:
-            lib.mla_cache_append(d["cache"], bt, lens, d["c_new"], d["kpe_new"])
-        lib.mla_absorb_q(d["q"], d["w_uk"], q_abs)
-        if timed:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-        lib.mla_decode(q_abs, d["cache"], bt, att, wl.scale, o_lat, lse, ws, args.splits)
-        if timed:
-            b.record(stream)
-            ev.append((a, b))
-        lib.mla_out_proj(o_lat, d["w_uv"], out)
-
-    def step(i, timed=False):
-        if layers > 1:
-            for l in range(layers):
-                one_layer(inst[l], timed)
-        else:
-            one_layer(inst[i % sets], timed)
-
-    print(f"bench: {wl.name}, {N} tokens per layer, {layers} layer(s), {sets} input set(s)",
-          file=sys.stderr, flush=True)
     if args.profile_run:
         for i in range(args.warmup):
-            step(i)
-        d = inst[0]
+            res.step(lib, i)
         for _ in range(args.steps):
-            lib.mla_decode(q_abs, d["cache"], bt, att, wl.scale, o_lat, lse, ws, args.splits)
+            res.decode(lib, res.inst[0])
         torch.cuda.synchronize()
-        del inst
+        del res
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(f"profile run done: {args.steps} mla_decode calls, one {CALIB_BYTES} B copy", file=sys.stderr,
-              flush=True)
+        say(f"profile run done: {args.steps} mla_decode calls, one {CALIB_BYTES} B copy")
         return
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_step = dt * 1e3 / args.steps
-    # The decode call's own time comes from a second pass of the same steps with HIP events around
-    # each mla_decode (event records between kernels lengthen a step, so they stay out of the pass
-    # above).
-    for i in range(args.steps):
-        step(i, timed=True)
-    torch.cuda.synchronize()
-    dec_times = sorted(a.elapsed_time(b) for a, b in ev)
-    dec_ms = sum(dec_times) / len(dec_times)
-    dec_median = dec_times[len(dec_times) // 2]
-    # Warm numbers, labelled: when the cache fits in the 256 MB Infinity Cache, the same input set
-    # every call (the steps above rotate sets so that each call reads HBM).
-    warm = None
-    if cache_bytes < MALL_BYTES and layers == 1:
-        d = inst[0]
-        for _ in range(3):
-            lib.mla_decode(q_abs, d["cache"], bt, att, wl.scale, o_lat, lse, ws, args.splits)
-        wev = []
-        for _ in range(args.steps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            lib.mla_decode(q_abs, d["cache"], bt, att, wl.scale, o_lat, lse, ws, args.splits)
-            b.record(stream)
-            wev.append((a, b))
-        torch.cuda.synchronize()
-        wms = sum(a.elapsed_time(b) for a, b in wev) / len(wev)
-        warm = {"label": "warm: one input set, cache resident in the Infinity Cache",
-                "ms_per_launch": round(wms, 5), "achieved": round(cache_bytes / (wms * 1e-3) / 1e9, 2)}
-    peaks = measured_peaks(dev)
 
+    main_rec = time_workload(lib, res, args.steps, args.warmup)
+    say(f"main workload timed: {main_rec['ms_per_step']} ms per step")
+    B, H, layers, N = wl.batch, wl.heads, wl.layers, wl.tokens
+    ms_step = main_rec["ms_per_step"]
     decode_flops = N * 2 * H * (D_C + D_R + D_C)
     proj_flops = 2 * 2 * B * H * D_NOPE * D_C
     step_flops = layers * (decode_flops + proj_flops)
-    step_cache = layers * cache_bytes
-    value = step_cache / (ms_step * 1e-3) / 1e9
-    dec_gbs = cache_bytes / (dec_ms * 1e-3) / 1e9
-    dec_tf = decode_flops / (dec_ms * 1e-3) / 1e12
-    traffic = traffic_record(wl.name)
+    value = layers * res.cache_bytes / (ms_step * 1e-3) / 1e9
+    side = {}
+    if layers == 1:
+        side = side_records(lib, synth, res, dev, args.steps,
+                            ("sparse_topk", "fp6", "out_proj_hidden", "producer"))
+    del res
+    torch.cuda.empty_cache()
+    peaks = measured_peaks(dev)
+    dc = main_rec["decode_call"]
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded counter-based draws, bf16)",
         "config": {"workload": wl.name, "batch": B, "heads": H, "layers": layers,
-                   "attended_tokens_per_layer": N, "page_size": 64, "input_sets": sets,
-                   "step": ("append+" if wl.append else "") + "absorb+decode+merge+out_proj",
-                   "num_splits": args.splits or "auto"},
+                   "attended_tokens_per_layer": N, "page_size": 64, "input_sets": main_rec["input_sets"],
+                   "step": main_rec["step"], "num_splits": args.splits or "auto"},
         "tflops": round(step_flops / (ms_step * 1e-3) / 1e12, 3),
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "mla_decode (decode + merge kernels)", "bound": "hbm",
-                     "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else traffic["bytes_per_call"],
-                     "ms_per_launch": round(dec_ms, 5),
-                     "ms_per_launch_median": round(dec_median, 5),
-                     "mfma_tflops": round(dec_tf, 2),
-                     "mfma_frac": round(dec_tf / MFMA_BF16_PEAK_TF, 4),
-                     "measured_peaks": peaks,
-                     "frac_of_measured_copy": round(dec_gbs / peaks["hbm_copy_gbs"], 4),
-                     "mfma_frac_of_measured": round(dec_tf / peaks["mfma_bf16_tflops"], 4)},
+        "roofline": dict(dc, kernel="mla_decode (one call per layer)",
+                         measured_peaks=peaks,
+                         frac_of_measured_copy=round(dc["achieved"] / peaks["hbm_copy_gbs"], 4),
+                         mfma_frac_of_measured=round(dc["mfma_tflops"] / peaks["mfma_bf16_tflops"], 4)),
+        "calls_per_layer": main_rec["calls_per_layer"],
     }
-    if warm is not None:
-        line["roofline"]["warm"] = warm
-    if wl.append:  # the table has a slot at each sequence's next position only when the workload appends
-        line["producer"] = producer_timing(lib, synth, wl, dev, inst[0]["cache"], bt, lens, args.steps)
-    sp = sparse_timing(lib, synth, wl, dev, q_abs, bt, att, inst[0]["cache"], args.steps, dec_ms)
-    if sp is not None:
-        line["sparse_topk"] = sp
-    oh = out_hidden_timing(lib, synth, wl, dev, out, args.steps)
-    if oh is not None:
-        line["out_proj_hidden"] = oh
-    fp6 = fp6_timing(lib, synth, wl, dev, q_abs, bt, att, o_lat, lse, ws, args.steps, args.splits, dec_ms)
-    if fp6 is not None:
-        line["fp6"] = fp6
+    line["roofline"].pop("kernels", None)
+    line.update(side)
+    # The other workloads, each its own block: the long-context decode (4 x 131,072 tokens) with the
+    # further calls measured on it, the batched one (32 x 4,096) whose matrix-core fraction is the
+    # one to read, the 16-head one and the ragged one.
+    if not args.main_only:
+        for cfg in (3, 2, 4, 1):
+            if cfg == args.config:
+                continue
+            wl_c = bench_workload(cfg)
+            say(f"{wl_c.name}, {wl_c.tokens} tokens")
+            r = Resident(lib, synth, wl_c, dev, 0, args.splits)
+            rec = time_workload(lib, r, args.steps, args.warmup)
+            if cfg in (2, 3):
+                rec.update(side_records(lib, synth, r, dev, args.steps,
+                                        ("sparse_topk", "fp6") if cfg == 3 else
+                                        ("sparse_topk", "fp6", "out_proj_hidden", "producer")))
+            del r
+            torch.cuda.empty_cache()
+            line[f"c{cfg}"] = rec
     if not args.no_cpu_baseline:
+        say("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -30,6 +30,20 @@ def rel_err(gpu, ref) -> float:
     return float((num / den).max())
 
 
+def lse_err(gpu, ref) -> float:
+    """Largest absolute error of the log-sum-exp.  lse is a logarithm, so its absolute error is the
+    relative error of the softmax denominator; it is compared absolutely against the same 1e-2 /
+    1e-4 bounds.  Entries where the reference is -inf (empty sequences) must be -inf too."""
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    empty = np.isneginf(r)
+    if not np.array_equal(np.isneginf(g), empty):
+        return math.inf
+    if empty.all():
+        return 0.0
+    return float(np.abs(g[~empty] - r[~empty]).max())
+
+
 def to_host_f64(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return O.bf16_to_f64(t.view(torch.int16).cpu().numpy())

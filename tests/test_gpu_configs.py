@@ -12,7 +12,7 @@ import torch
 
 import synth
 from oracle import mla_oracle as O
-from tests.gpu_cases import BF16_TOL, F32_TOL, Gpu, host_inputs, pick, rel_err, say, to_host_f64
+from tests.gpu_cases import BF16_TOL, F32_TOL, Gpu, host_inputs, pick, lse_err, rel_err, say, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -60,8 +60,8 @@ def _check(lib, cfg, layer, n_seq, n_heads, f32):
     sel = np.ix_(seqs, heads)
     e_o = rel_err(o_gpu[sel], o_ref[sel])
     e_out = rel_err(out_gpu[sel], out_ref[sel])
-    e_l = float(np.abs(lse_gpu[sel] - lse_ref[sel]).max() / np.abs(lse_ref[sel]).max())
-    e_l2 = float(np.abs(lse2_gpu[sel] - lse2_ref[sel]).max() / np.abs(lse2_ref[sel]).max())
+    e_l = lse_err(lse_gpu[sel], lse_ref[sel])
+    e_l2 = lse_err(lse2_gpu[sel], lse2_ref[sel])
     say(f"  o_lat {e_o:.2e}  out {e_out:.2e}  lse {e_l:.2e} / {e_l2:.2e}  ({len(seqs)} seq x {len(heads)} heads)")
     tol = F32_TOL if f32 else BF16_TOL
     assert e_o <= tol and e_out <= tol and e_l <= tol and e_l2 <= tol

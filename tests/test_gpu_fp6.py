@@ -8,7 +8,7 @@ import torch
 
 import synth
 from oracle import mla_oracle as O
-from tests.gpu_cases import BF16_TOL, Gpu, host_inputs, pick, rel_err, say, to_host_f64
+from tests.gpu_cases import BF16_TOL, Gpu, host_inputs, pick, lse_err, rel_err, say, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -123,8 +123,7 @@ def _decode_case(lib, wl, splits=0, seqs=None, heads=None):
     o = to_host_f64(g.o_lat)
     e_o = rel_err(o[sel], o_ref[sel])
     lse = g.lse.cpu().numpy()
-    fin = np.isfinite(lse_ref[sel])
-    e_l = float(np.abs(lse[sel][fin] - lse_ref[sel][fin]).max() / np.abs(lse_ref[sel][fin]).max()) if fin.any() else 0.0
+    e_l = lse_err(lse[sel], lse_ref[sel])
     return e_o, e_l, g
 
 
@@ -214,6 +213,6 @@ def test_full_size(lib, cfg, n_seq, n_heads):
                                                wl.scale, batch=seqs, heads=heads)
     sel = np.ix_(seqs, heads)
     e_o = rel_err(o[sel], o_ref[sel])
-    e_l = float(np.abs(lse[sel] - lse_ref[sel]).max() / np.abs(lse_ref[sel]).max())
+    e_l = lse_err(lse[sel], lse_ref[sel])
     say(f"  o_lat err {e_o:.3e}  lse err {e_l:.3e}")
     assert e_o <= BF16_TOL and e_l <= BF16_TOL

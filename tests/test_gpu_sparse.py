@@ -9,7 +9,7 @@ import torch
 
 import synth
 from oracle import mla_oracle as O
-from tests.gpu_cases import BF16_TOL, Gpu, host_inputs, pick, rel_err, say, to_host_f64
+from tests.gpu_cases import BF16_TOL, Gpu, host_inputs, pick, lse_err, rel_err, say, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -120,7 +120,7 @@ def test_gathered_rows_and_sparse_decode(lib):
     assert torch.all(g.o_lat[0].float() == 0) and torch.all(torch.isneginf(g.lse[0]))
     e_o = rel_err(o[1:], o_ref[1:])
     lse = g.lse.cpu().numpy()
-    e_l = float(np.abs(lse[1:] - lse_ref[1:]).max() / np.abs(lse_ref[1:]).max())
+    e_l = lse_err(lse[1:], lse_ref[1:])
     say(f"  o_lat err {e_o:.3e}  lse err {e_l:.3e}")
     assert e_o <= BF16_TOL and e_l <= BF16_TOL
 
@@ -210,7 +210,7 @@ def test_decode_topk_matches_gather(lib, heads, k):
     sel = np.ix_(list(seqs), hd)
     e_o = rel_err(to_host_f64(o)[sel], o_ref[sel])
     lse_np = lse.cpu().numpy()
-    e_l = float(np.abs(lse_np[sel] - lse_ref[sel]).max() / np.abs(lse_ref[sel]).max())
+    e_l = lse_err(lse_np[sel], lse_ref[sel])
     say(f"  o_lat err {e_o:.3e}  lse err {e_l:.3e}")
     assert e_o <= BF16_TOL and e_l <= BF16_TOL
 

@@ -181,6 +181,7 @@ def test_latent_decode_vs_brute_force():
     q_abs = O.absorb_batch(q, w_uk)
     o_lat, lse = O.latent_decode_batch(q_abs, cache, bt, lens, 0.5, d_c=d_c)
     page = cache.shape[1]
+    # q_abs itself was pinned by its own brute-force test below; here it is only an input
     for b in range(len(lens)):
         for h in range(q.shape[1]):
             s = []
@@ -613,3 +614,54 @@ def test_sparse_decode_with_k_at_least_the_length_is_dense():
     o2, l2 = O.latent_decode_batch(q, cache, bt, lens, 0.05)
     assert np.array_equal(o, o2) and np.array_equal(l, l2)
     assert chosen[0].tolist() == list(range(100))
+
+
+# --------------------------------------------------------------------------------------------------
+# The batched absorption and up-projection (explainer Step 6) against explicit loops
+# --------------------------------------------------------------------------------------------------
+
+def _tiny_proj(seed):
+    """Batch 3, heads 2, d_nope 3, d_R 2, d_c 5, d_v 4: every axis a different length, so a swapped
+    batch/head index, a transposed weight or a misplaced q^R strip changes the shape or the values."""
+    rng = np.random.default_rng(seed)
+    B, H, d_nope, d_r, d_c, d_v = 3, 2, 3, 2, 5, 4
+    q = rng.normal(size=(B, H, d_nope + d_r))
+    w_uk = rng.normal(size=(H, d_nope, d_c))
+    o_lat = rng.normal(size=(B, H, d_c))
+    w_uv = rng.normal(size=(H, d_c, d_v))
+    return q, w_uk, o_lat, w_uv
+
+
+def test_absorb_batch_vs_explicit_loops():
+    """q_abs[b][h][j] = sum_i q[b][h][i] W_UK[h][i][j] for j < d_c, then q^R copied: the content
+    query moved into latent space (explainer Step 6), the RoPE strip untouched (Step 7)."""
+    q, w_uk, _, _ = _tiny_proj(11)
+    B, H, _ = q.shape
+    d_nope, d_c = w_uk.shape[1:]
+    got = O.absorb_batch(q, w_uk)
+    assert got.shape == (B, H, d_c + q.shape[2] - d_nope)
+    for b in range(B):
+        for h in range(H):
+            for j in range(d_c):
+                want = sum(q[b][h][i] * w_uk[h][i][j] for i in range(d_nope))
+                assert abs(got[b, h, j] - want) < 1e-12, (b, h, j)
+            for r in range(q.shape[2] - d_nope):
+                assert got[b, h, d_c + r] == q[b][h][d_nope + r]
+    # a selection computes the same entries and leaves the rest NaN
+    part = O.absorb_batch(q, w_uk, batch=[2], heads=[1])
+    assert np.array_equal(part[2, 1], got[2, 1])
+    assert np.isnan(part[0]).all() and np.isnan(part[2, 0]).all()
+
+
+def test_out_proj_batch_vs_explicit_loops():
+    """out[b][h][k] = sum_j o_lat[b][h][j] W_UV[h][j][k] (explainer Step 6: W^UV after the sum)."""
+    _, _, o_lat, w_uv = _tiny_proj(12)
+    B, H, d_c = o_lat.shape
+    d_v = w_uv.shape[2]
+    got = O.out_proj_batch(o_lat, w_uv)
+    assert got.shape == (B, H, d_v)
+    for b in range(B):
+        for h in range(H):
+            for k in range(d_v):
+                want = sum(o_lat[b][h][j] * w_uv[h][j][k] for j in range(d_c))
+                assert abs(got[b, h, k] - want) < 1e-12, (b, h, k)
