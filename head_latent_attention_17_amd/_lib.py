@@ -17,12 +17,13 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_BF16, MLA_F32 = 0, 1
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
           -4: "MLA_ERR_WORKSPACE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_BLOCK_TABLE",
-          -7: "MLA_ERR_HIP"}
+          -7: "MLA_ERR_HIP", -8: "MLA_ERR_SCRATCH"}
 EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", "mla_cache_append",
            "mla_absorb_q", "mla_decode", "mla_out_proj", "mla_cache_append_hidden_workspace_size",
            "mla_cache_append_hidden", "mla_cache_append_fp6", "mla_cache_quantize_fp6", "mla_decode_fp6",
            "mla_out_proj_hidden_workspace_size", "mla_out_proj_hidden", "mla_index_topk_workspace_size",
-           "mla_index_topk", "mla_gather_rows", "mla_decode_topk_workspace_size", "mla_decode_topk")
+           "mla_index_topk", "mla_gather_rows", "mla_decode_topk_workspace_size", "mla_decode_topk", "mla_decode_noalloc_max_bytes",
+           "mla_decode_noalloc")
 INDEX_DIM = 128          # MLA_INDEX_DIM: int8 numbers in a token's index vector
 FP6_PAGE_BYTES = 27904   # MLA_FP6_PAGE_BYTES: 64 rows of 432 code bytes, then 64 float32 scales
 
@@ -44,6 +45,10 @@ lib.mla_absorb_q.restype = _i
 lib.mla_absorb_q.argtypes = [_p, _p, _p, _i, _i, _i, _p]
 lib.mla_decode.restype = _i
 lib.mla_decode.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _p, _sz, _i, _i, _p]
+lib.mla_decode_noalloc_max_bytes.restype = _sz
+lib.mla_decode_noalloc_max_bytes.argtypes = []
+lib.mla_decode_noalloc.restype = _i
+lib.mla_decode_noalloc.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _i, _i, _p]
 lib.mla_out_proj.restype = _i
 lib.mla_out_proj.argtypes = [_p, _p, _p, _i, _i, _i, _p]
 lib.mla_cache_append_hidden_workspace_size.restype = _sz
@@ -203,6 +208,21 @@ def mla_decode(q_abs, kv_cache, block_table, seq_lens, softmax_scale, o_lat, lse
                           _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, H,
                           float(softmax_scale), _ptr(o_lat), _ptr(lse), _ptr(workspace), ws_bytes,
                           int(num_splits), _dtype_of(q_abs), _stream(stream)), "mla_decode")
+
+
+def mla_decode_noalloc_max_bytes() -> int:
+    return int(lib.mla_decode_noalloc_max_bytes())
+
+
+def mla_decode_noalloc(q_abs, kv_cache, block_table, seq_lens, softmax_scale, o_lat, lse=None, num_splits=0,
+                       stream=None):
+    """mla_decode with the library's fixed scratch array in place of a workspace (allocates nothing)."""
+    _dev(q_abs, kv_cache, block_table, seq_lens, o_lat, lse)
+    B, H = q_abs.shape[0], q_abs.shape[1]
+    _check(lib.mla_decode_noalloc(_ptr(q_abs), _ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1],
+                                  _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, H,
+                                  float(softmax_scale), _ptr(o_lat), _ptr(lse), int(num_splits),
+                                  _dtype_of(q_abs), _stream(stream)), "mla_decode_noalloc")
 
 
 def mla_out_proj(o_lat, w_uv, out, stream=None):

@@ -54,11 +54,12 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: page_size must be 64, heads in {16,32,64,128} (64 or 128 and bf16 for the ~6-bit cache, 32 to 128 for mla_decode_topk)";
     case MLA_ERR_BLOCK_TABLE: return "MLA_ERR_BLOCK_TABLE: block table entry out of range";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch failed";
+    case MLA_ERR_SCRATCH: return "MLA_ERR_SCRATCH: these sizes need more scratch than mla_decode_noalloc's fixed device buffer holds";
     default: return "unknown mla_status";
   }
 }
 
-int mla_abi_version(void) { return 105; }
+int mla_abi_version(void) { return 106; }
 
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype) {
@@ -141,11 +142,12 @@ mla_status mla_out_proj(const void* o_lat, const void* w_uv, void* out, int batc
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+// workspace == nullptr with noalloc: the library's fixed scratch array stands in for the workspace.
 static mla_status decode_common(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
                                 const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
                                 int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
                                 void* workspace, size_t workspace_bytes_given, int num_splits, mla_dtype dtype,
-                                bool fp6, hipStream_t stream) {
+                                bool fp6, hipStream_t stream, bool noalloc = false) {
   if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
   if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
   if (!valid_heads(num_heads)) return MLA_ERR_UNSUPPORTED;
@@ -156,7 +158,12 @@ static mla_status decode_common(const void* q_abs, const void* kv_cache, int num
   if (!q_abs || !kv_cache || !block_table || !seq_lens || !o_lat) return MLA_ERR_NULL;
   const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq);
   const size_t need = workspace_bytes(batch, num_heads, units);
-  if (!workspace || workspace_bytes_given < need) return MLA_ERR_WORKSPACE;
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes) return MLA_ERR_SCRATCH;
+    if (noalloc_scratch(&workspace) != hipSuccess) return MLA_ERR_HIP;
+  } else if (!workspace || workspace_bytes_given < need) {
+    return MLA_ERR_WORKSPACE;
+  }
   if (debug_checks_enabled()) {
     bool bad = false;
     if (check_tables(block_table, max_blocks_per_seq, seq_lens, batch, num_pages, false, stream, &bad) != hipSuccess)
@@ -196,6 +203,16 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
   return decode_common(q_abs, kv_cache, num_pages, page_size, block_table, max_blocks_per_seq, seq_lens, batch,
                        num_heads, softmax_scale, o_lat, lse, workspace, workspace_bytes_given, num_splits, dtype,
                        false, stream);
+}
+
+size_t mla_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+mla_status mla_decode_noalloc(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                              const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                              int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
+                              int num_splits, mla_dtype dtype, hipStream_t stream) {
+  return decode_common(q_abs, kv_cache, num_pages, page_size, block_table, max_blocks_per_seq, seq_lens, batch,
+                       num_heads, softmax_scale, o_lat, lse, nullptr, 0, num_splits, dtype, false, stream, true);
 }
 
 mla_status mla_decode_fp6(const void* q_abs, const void* kv_cache6, int num_pages, int page_size,

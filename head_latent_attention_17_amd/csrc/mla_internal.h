@@ -18,6 +18,7 @@ constexpr int kNumCUs = 256;  // MI355X compute units (used only to pick the aut
 constexpr int kAppendChunks = 20;  // 5,120 / 256: partial sums per output of the producer products
 constexpr int kFp6RowBytes = kRow * 6 / 8;                       // 432: a row of 6-bit codes
 constexpr int kFp6PageBytes = kPage * kFp6RowBytes + kPage * 4;  // 27,904: rows, then fp32 scales
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;       // mla_decode_noalloc's fixed scratch
 
 // Everything a decode launch needs.  Pointers are device pointers.
 struct DecodeParams {
@@ -94,6 +95,9 @@ hipError_t check_positions(const int32_t* block_table, int max_blocks, const int
 // (append = true); synchronises s.  *bad is set when an entry is out of range.
 hipError_t check_tables(const int32_t* block_table, int max_blocks, const int32_t* lens, int batch,
                         int num_pages, bool append, hipStream_t s, bool* bad);
+// Device address of this device's fixed scratch array (kNoAllocScratchBytes), looked up on the first
+// call on each device; allocates nothing.
+hipError_t noalloc_scratch(void** out);
 // MLA_DEBUG_CHECKS=1 in the environment, read at every call.
 bool debug_checks_enabled();
 

@@ -33,7 +33,8 @@
  *
  * Conventions:
  *   - Every call is asynchronous on the caller's stream (0 = the null stream).  The library never
- *     synchronises and never allocates; scratch memory comes from a caller workspace.
+ *     synchronises and never allocates; scratch memory comes from a caller workspace (for
+ *     mla_decode_noalloc, from a fixed device array inside the library).
  *   - Every entry point validates its arguments on the host before launching anything and returns a
  *     negative mla_status on error, without touching any buffer.  Launch failures are reported as
  *     MLA_ERR_HIP.  Nothing is thrown across the ABI.
@@ -65,7 +66,8 @@ typedef enum {
   MLA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than mla_decode_workspace_size() */
   MLA_ERR_UNSUPPORTED = -5,  /* page_size != 64, or heads not in {16, 32, 64, 128} */
   MLA_ERR_BLOCK_TABLE = -6,  /* device-side check (MLA_DEBUG_CHECKS=1): bad table entry or length */
-  MLA_ERR_HIP = -7           /* a HIP launch failed */
+  MLA_ERR_HIP = -7,          /* a HIP launch failed */
+  MLA_ERR_SCRATCH = -8       /* mla_decode_noalloc: the sizes need more than its fixed scratch buffer */
 } mla_status;
 
 typedef enum { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
@@ -152,6 +154,25 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
                       int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
                       void* workspace, size_t workspace_bytes, int num_splits, mla_dtype dtype,
                       hipStream_t stream);
+
+/*
+ * mla_decode without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments, results and
+ * errors are those of mla_decode, minus workspace and workspace_bytes: the scratch space comes from
+ * a fixed device array inside the library, mla_decode_noalloc_max_bytes() bytes (128 MiB) on every
+ * GPU the library runs on, held from the moment the library's code is loaded on that GPU until the
+ * process ends.  Sizes whose mla_decode_workspace_size() exceeds it return MLA_ERR_SCRATCH before
+ * anything is launched (at 128 heads and the automatic split: up to 253 sequences).  The call
+ * allocates nothing; its first call on a device looks up that device's array once.  Every call on
+ * one GPU shares that GPU's array: calls that may overlap on one GPU (two streams, two threads)
+ * race and must be ordered by the caller.  No part of the array needs to start at zero; each call
+ * writes what it later reads.  Results are bit-identical to mla_decode's for equal arguments.
+ */
+size_t mla_decode_noalloc_max_bytes(void);
+mla_status mla_decode_noalloc(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                              const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                              int batch, int num_heads, float softmax_scale, void* o_lat, float* lse,
+                              int num_splits, mla_dtype dtype, hipStream_t stream);
 
 /*
  * The ~6-bit cache (explainer, the audit after Step 8: deployed V2 keeps each cached number in about

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.mla_abi_version() == 105
+    assert L.mla_abi_version() == 106
     for code, name in L.STATUS.items():
         assert L.mla_status_string(code).startswith(name)
     assert "unknown" in L.mla_status_string(12345)
@@ -261,3 +261,26 @@ def test_decode_topk_validation():
     assert call(15, ws - 1) == -4
     assert f(None, None, 0, 64, None, 4, None, None, 0, 100, 128, 0.1, None, None, None, 0, None) == 0
 
+
+
+def test_decode_noalloc_validation():
+    """The no-allocation decode validates like mla_decode and rejects sizes whose workspace would
+    exceed its fixed scratch array before any HIP call."""
+    L = _lib()
+    assert L.mla_decode_noalloc_max_bytes() == 128 << 20
+
+    def call(batch=1, heads=128, max_blocks=16, splits=0, page_size=64, dtype=0, q=FAKE):
+        return L.lib.mla_decode_noalloc(q, FAKE, 16, page_size, FAKE, max_blocks, FAKE, batch, heads, 0.07,
+                                        FAKE, None, splits, dtype, None)
+
+    assert call(batch=300, max_blocks=64) == -8          # (256 + 300) x 128 x 2,056 B > 128 MiB
+    assert call(batch=254, max_blocks=64) == -8
+    # the documented limit: 253 sequences at 128 heads and the automatic split (256 ranges)
+    assert L.mla_decode_workspace_size(253, 128, 64, 0) <= L.mla_decode_noalloc_max_bytes()
+    assert L.mla_decode_workspace_size(254, 128, 64, 0) > L.mla_decode_noalloc_max_bytes()
+    assert call(page_size=32) == -5
+    assert call(heads=100) == -5
+    assert call(dtype=3) == -3
+    assert call(batch=-1) == -2
+    assert call(q=None) == -1
+    assert call(batch=0) == 0
