@@ -1,8 +1,10 @@
 """Benchmark: MLA decode steps over a paged latent cache on one MI355X.
 
-A step is the whole path for one batch and every layer: query absorption through W_UK, latent
-decode attention (with its split merge) and the W_UV out-projection, plus the cache append of one
-new row per sequence in the one-layer workloads.  Inputs are seeded synthetic data resident in HBM
+A step is the whole path for one batch and every layer: query absorption through W_UK (mla_absorb_q),
+then latent decode attention with its split merge and the W_UV out-projection in one call
+(mla_decode_out_proj: the decode kernel, then one kernel for the merge and the projection), plus the
+cache append of one new row per sequence in the one-layer workloads.  The same steps with the decode
+and the out-projection as two calls (mla_decode, mla_out_proj) are timed beside them.  Inputs are seeded synthetic data resident in HBM
 before timing starts.
 
 Default workload (the headline line): the full 60-layer decode step, 64 sequences with cached
@@ -14,7 +16,8 @@ step time), from K steps timed between two synchronisations with nothing else on
 `roofline` reports the dominant call, mla_decode, timed with HIP events on the launch stream in a
 second pass of the same K steps (mean and median per layer call), against the datasheet peaks and
 against what this GPU measures on plain library work (a device copy, a bf16 matrix product).
-`calls_per_layer` gives the other calls of a layer the same way.
+`calls_per_layer` gives the calls of a layer the same way (the fused call against its algorithmic
+bytes: cache, W_UV and the output rows).
 
 Blocks `c3`, `c2`, `c4`, `c1` time the other workloads the same way (a whole step, then each call):
 4 x 131,072 tokens (the long-context decode), 32 x 4,096 (the batched decode whose matrix-core
@@ -68,8 +71,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
-                    help="for counter runs: a few untimed steps, then mla_decode alone, then one "
-                         "1 GiB device copy that calibrates the byte counters; prints no JSON")
+                    help="for counter runs: a few untimed steps, then mla_decode alone, then "
+                         "mla_decode_out_proj, then one 1 GiB device copy that calibrates the byte "
+                         "counters; prints no JSON")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of "
                          "--profile-run into profiles/traffic_<workload>.json; needs no GPU")
@@ -414,7 +418,8 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str):
         scale = CALIB_BYTES / calib
         total = 0.0
         for tag in ("decode_mfma_kernel", "merge"):
-            vals = [float(r["Counter_Value"]) * 1024 for r in rows if tag in r["Kernel_Name"]]
+            vals = [float(r["Counter_Value"]) * 1024 for r in rows
+                    if tag in r["Kernel_Name"] and "out_proj" not in r["Kernel_Name"]]
             if not vals:
                 raise SystemExit(f"{counter}: no {tag} dispatch in {folder}")
             avg = sum(vals) / len(vals) * scale
@@ -473,16 +478,19 @@ class Resident:
         self.o_lat = torch.empty(B, H, D_C, dtype=torch.bfloat16, device=dev)
         self.out = torch.empty(B, H, D_V, dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(B, H, dtype=torch.float32, device=dev)
-        self.ws = torch.empty(lib.mla_decode_workspace_size(B, H, wl.max_blocks, splits), dtype=torch.uint8,
-                              device=dev)
+        self.ws = torch.empty(lib.mla_decode_out_proj_workspace_size(B, H, wl.max_blocks, splits),
+                              dtype=torch.uint8, device=dev)
 
     def decode(self, lib, d):
         wl = self.wl
         lib.mla_decode(self.q_abs, d["cache"], self.bt, self.att, wl.scale, self.o_lat, self.lse, self.ws,
                        self.splits)
 
-    def layer(self, lib, d, marks=None):
-        """One layer of the step; with `marks` (five events) each call is bracketed on the stream."""
+    def layer(self, lib, d, marks=None, separate=False):
+        """One layer of the step: append (one-layer workloads), absorb, then the decode with its merge
+        and the W_UV projection in one call (mla_decode_out_proj), or with `separate` as the two calls
+        mla_decode and mla_out_proj.  With `marks` (four events) each call is bracketed on the
+        stream."""
         wl = self.wl
         if marks: marks[0].record()
         if wl.append:
@@ -490,26 +498,31 @@ class Resident:
         if marks: marks[1].record()
         lib.mla_absorb_q(d["q"], d["w_uk"], self.q_abs)
         if marks: marks[2].record()
-        self.decode(lib, d)
+        if separate:
+            self.decode(lib, d)
+            lib.mla_out_proj(self.o_lat, d["w_uv"], self.out)
+        else:
+            lib.mla_decode_out_proj(self.q_abs, d["cache"], self.bt, self.att, wl.scale, d["w_uv"], self.out,
+                                    None, None, self.ws, self.splits)
         if marks: marks[3].record()
-        lib.mla_out_proj(self.o_lat, d["w_uv"], self.out)
-        if marks: marks[4].record()
 
-    def step(self, lib, i, marks_out=None):
+    def step(self, lib, i, marks_out=None, separate=False):
         import torch
         ds = self.inst[:self.layers] if self.layers > 1 else [self.inst[i % self.sets]]
         for d in ds:
             marks = None
             if marks_out is not None:
-                marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
                 marks_out.append(marks)
-            self.layer(lib, d, marks)
+            self.layer(lib, d, marks, separate)
 
 
 def time_workload(lib, res: Resident, steps: int, warmup: int) -> dict:
-    """Whole steps between two synchronisations (nothing but the path's kernels on the stream), then
-    a second pass of the same steps with HIP events around every call of every layer, on the stream
-    the calls are launched on (torch's current stream, which the binding passes to the library)."""
+    """Whole steps between two synchronisations (nothing but the path's kernels on the stream); a
+    second pass of the same steps with HIP events around every call of every layer, on the stream
+    the calls are launched on (torch's current stream, which the binding passes to the library);
+    then mla_decode alone (decode + merge kernels, the call the roofline reports) between events on
+    the same inputs; then the same steps with the decode and the out-projection as two calls."""
     import torch
     wl = res.wl
     for i in range(warmup):
@@ -525,29 +538,68 @@ def time_workload(lib, res: Resident, steps: int, warmup: int) -> dict:
         res.step(lib, i, marks)
     torch.cuda.synchronize()
     per_call = {}
-    for k, name in enumerate(("append", "absorb", "decode", "out_proj")):
+    for k, name in enumerate(("append", "absorb", "decode_out_proj")):
         ts = sorted(m[k].elapsed_time(m[k + 1]) for m in marks)
         per_call[name] = (sum(ts) / len(ts), ts[len(ts) // 2])
+    # mla_decode alone, every layer / rotation set in turn
+    ds = res.inst[:res.layers] if res.layers > 1 else res.inst[:res.sets]
+    ev = []
+    for i in range(max(steps, 1) * (res.layers if res.layers > 1 else 1)):
+        d = ds[i % len(ds)]
+        lib.mla_absorb_q(d["q"], d["w_uk"], res.q_abs)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        res.decode(lib, d)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    dec_ms, dec_med = sum(ts) / len(ts), ts[len(ts) // 2]
+    # the same steps with mla_decode and mla_out_proj as separate calls, against the one-call form in
+    # alternating blocks (so that clock drift falls on both alike); medians of three blocks each
+    blocks = {False: [], True: []}
+    for rnd in range(3):
+        for sep in (True, False):
+            res.step(lib, 0, separate=sep)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                res.step(lib, i, separate=sep)
+            torch.cuda.synchronize()
+            blocks[sep].append((time.perf_counter() - t0) * 1e3 / steps)
+    ms_sep = sorted(blocks[True])[1]
+    ms_one = sorted(blocks[False])[1]
+
     N = wl.tokens
-    dec_ms, dec_med = per_call["decode"]
     decode_flops = N * 2 * wl.heads * (D_C + D_R + D_C)
+    proj_flops = 2 * wl.batch * wl.heads * D_NOPE * D_C
     dec_gbs = res.cache_bytes / (dec_ms * 1e-3) / 1e9
     dec_tf = decode_flops / (dec_ms * 1e-3) / 1e12
     traffic = traffic_record(wl.name)
-    calls = {"decode": {"ms_per_launch": round(dec_ms, 5), "ms_per_launch_median": round(dec_med, 5)}}
     wbytes = wl.heads * D_NOPE * D_C * 2
-    for name in ("absorb", "out_proj"):
-        ms = per_call[name][0]
-        calls[name] = {"ms_per_launch": round(ms, 5), "weight_gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
-                       "weight_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    f_ms, f_med = per_call["decode_out_proj"]
+    f_bytes = res.cache_bytes + wbytes + wl.batch * wl.heads * D_V * 2
+    f_gbs = f_bytes / (f_ms * 1e-3) / 1e9
+    calls = {"decode_out_proj": {"ms_per_launch": round(f_ms, 5), "ms_per_launch_median": round(f_med, 5),
+                                 "bytes": f_bytes, "achieved": round(f_gbs, 2), "unit": "GB/s",
+                                 "frac": round(f_gbs / HBM_PEAK_GBS, 4),
+                                 "mfma_tflops": round((decode_flops + proj_flops) / (f_ms * 1e-3) / 1e12, 2)}}
+    ms = per_call["absorb"][0]
+    abytes = wbytes + wl.batch * wl.heads * (D_NOPE + D_R + D_C + D_R) * 2
+    calls["absorb"] = {"ms_per_launch": round(ms, 5), "bytes": abytes,
+                       "achieved": round(abytes / (ms * 1e-3) / 1e9, 1),
+                       "frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if wl.append:
         calls["append"] = {"ms_per_launch": round(per_call["append"][0], 5)}
     out = {
         "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "layers": res.layers,
         "attended_tokens_per_layer": N, "input_sets": res.sets, "ms_per_step": round(ms_step, 5),
-        "step": ("append+" if wl.append else "") + "absorb+decode+out_proj",
-        "decode_call": {"kernels": "mla_decode", "bound": "hbm", "achieved": round(dec_gbs, 2),
-                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "step": ("append+" if wl.append else "") + "absorb+decode_out_proj",
+        "ms_per_step_separate_calls": round(ms_sep, 5),
+        "ms_per_step_one_call_alternating": round(ms_one, 5),
+        "decode_call": {"kernels": "mla_decode (decode + merge kernels)", "bound": "hbm",
+                        "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                         "traffic": None if traffic is None else traffic["bytes_per_call"],
                         "ms_per_launch": round(dec_ms, 5), "ms_per_launch_median": round(dec_med, 5),
                         "mfma_tflops": round(dec_tf, 2), "mfma_frac": round(dec_tf / MFMA_BF16_PEAK_TF, 4)},
@@ -641,15 +693,19 @@ def main():
     if args.profile_run:
         for i in range(args.warmup):
             res.step(lib, i)
+        d = res.inst[0]
         for _ in range(args.steps):
-            res.decode(lib, res.inst[0])
+            res.decode(lib, d)
+        for _ in range(args.steps):
+            lib.mla_decode_out_proj(res.q_abs, d["cache"], res.bt, res.att, wl.scale, d["w_uv"], res.out, None,
+                                    None, res.ws, res.splits)
         torch.cuda.synchronize()
         del res
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        say(f"profile run done: {args.steps} mla_decode calls, one {CALIB_BYTES} B copy")
+        say(f"profile run done: {args.steps} mla_decode and mla_decode_out_proj calls, one {CALIB_BYTES} B copy")
         return
 
     main_rec = time_workload(lib, res, args.steps, args.warmup)
@@ -679,11 +735,13 @@ def main():
         "tflops": round(step_flops / (ms_step * 1e-3) / 1e12, 3),
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "roofline": dict(dc, kernel="mla_decode (one call per layer)",
+        "roofline": dict(dc, kernel="mla_decode (decode + merge kernels, one call per layer)",
                          measured_peaks=peaks,
                          frac_of_measured_copy=round(dc["achieved"] / peaks["hbm_copy_gbs"], 4),
                          mfma_frac_of_measured=round(dc["mfma_tflops"] / peaks["mfma_bf16_tflops"], 4)),
         "calls_per_layer": main_rec["calls_per_layer"],
+        "ms_per_step_separate_calls": main_rec["ms_per_step_separate_calls"],
+        "ms_per_step_one_call_alternating": main_rec["ms_per_step_one_call_alternating"],
     }
     line["roofline"].pop("kernels", None)
     line.update(side)

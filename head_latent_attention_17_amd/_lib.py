@@ -23,7 +23,7 @@ EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", 
            "mla_cache_append_hidden", "mla_cache_append_fp6", "mla_cache_quantize_fp6", "mla_decode_fp6",
            "mla_out_proj_hidden_workspace_size", "mla_out_proj_hidden", "mla_index_topk_workspace_size",
            "mla_index_topk", "mla_gather_rows", "mla_decode_topk_workspace_size", "mla_decode_topk", "mla_decode_noalloc_max_bytes",
-           "mla_decode_noalloc")
+           "mla_decode_noalloc", "mla_decode_out_proj_workspace_size", "mla_decode_out_proj")
 INDEX_DIM = 128          # MLA_INDEX_DIM: int8 numbers in a token's index vector
 FP6_PAGE_BYTES = 27904   # MLA_FP6_PAGE_BYTES: 64 rows of 432 code bytes, then 64 float32 scales
 
@@ -49,6 +49,10 @@ lib.mla_decode_noalloc_max_bytes.restype = _sz
 lib.mla_decode_noalloc_max_bytes.argtypes = []
 lib.mla_decode_noalloc.restype = _i
 lib.mla_decode_noalloc.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _i, _i, _p]
+lib.mla_decode_out_proj_workspace_size.restype = _sz
+lib.mla_decode_out_proj_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+lib.mla_decode_out_proj.restype = _i
+lib.mla_decode_out_proj.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _p, _p, _p, _sz, _i, _i, _p]
 lib.mla_out_proj.restype = _i
 lib.mla_out_proj.argtypes = [_p, _p, _p, _i, _i, _i, _p]
 lib.mla_cache_append_hidden_workspace_size.restype = _sz
@@ -223,6 +227,25 @@ def mla_decode_noalloc(q_abs, kv_cache, block_table, seq_lens, softmax_scale, o_
                                   _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, H,
                                   float(softmax_scale), _ptr(o_lat), _ptr(lse), int(num_splits),
                                   _dtype_of(q_abs), _stream(stream)), "mla_decode_noalloc")
+
+
+def mla_decode_out_proj_workspace_size(batch: int, num_heads: int, max_blocks_per_seq: int,
+                                       num_splits: int = 0, dtype: int = MLA_BF16) -> int:
+    return int(lib.mla_decode_out_proj_workspace_size(batch, num_heads, max_blocks_per_seq, num_splits, dtype))
+
+
+def mla_decode_out_proj(q_abs, kv_cache, block_table, seq_lens, softmax_scale, w_uv, out, o_lat=None, lse=None,
+                        workspace=None, num_splits=0, stream=None):
+    """mla_decode then mla_out_proj in one call: out [B][H][128] from q_abs [B][H][576] through
+    w_uv [H][512][128]; o_lat and lse written when given."""
+    _dev(q_abs, kv_cache, block_table, seq_lens, w_uv, out, o_lat, lse, workspace)
+    B, H = q_abs.shape[0], q_abs.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.mla_decode_out_proj(_ptr(q_abs), _ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1],
+                                   _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, H,
+                                   float(softmax_scale), _ptr(w_uv), _ptr(out), _ptr(o_lat), _ptr(lse),
+                                   _ptr(workspace), ws_bytes, int(num_splits), _dtype_of(q_abs),
+                                   _stream(stream)), "mla_decode_out_proj")
 
 
 def mla_out_proj(o_lat, w_uv, out, stream=None):

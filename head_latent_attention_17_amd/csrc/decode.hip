@@ -12,7 +12,6 @@
 namespace mla {
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s);
-bool mfma_supported(const DecodeParams& p);
 
 namespace {
 
@@ -161,38 +160,6 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
       *reinterpret_cast<float2*>(o + 64 * j + 2 * j32) = make_float2(acc[2 * j], acc[2 * j + 1]);
     if (j32 == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_run, l_run);
   }
-}
-
-// Units that hold sequence b: [wf, wl], from the table the matrix-core kernel writes, else derived
-// from seq_lens.  A unit in that range holds no page (and wrote nothing) only when there are more
-// units than pages.
-struct SeqUnits {
-  int wf, wl, W;
-  bool all_live;
-  long long P;
-  __device__ __forceinline__ bool live(int w) const {
-    return all_live || unit_start(P, W, w) != unit_start(P, W, w + 1);
-  }
-};
-
-__device__ __forceinline__ SeqUnits seq_units_of(const DecodeParams& p, int b, long long np) {
-  SeqUnits u;
-  u.W = p.num_units;
-  u.P = 0;
-  if (p.seq_units) {
-    const int4 d = *reinterpret_cast<const int4*>(p.seq_units + 4 * b);
-    u.wf = d.x;
-    u.wl = d.y;
-    u.all_live = d.z != 0;
-    if (!u.all_live) u.P = total_pages(p.seq_lens, p.batch);
-  } else {
-    u.P = total_pages(p.seq_lens, p.batch);
-    const long long before = pages_before(p.seq_lens, b);
-    u.wf = unit_of_page(u.P, u.W, before);
-    u.wl = unit_of_page(u.P, u.W, before + np - 1);
-    u.all_live = u.P >= u.W;
-  }
-  return u;
 }
 
 // Eight consecutive outputs from one lane (one 16-byte store for bf16, two for fp32).
@@ -438,33 +405,33 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& params, bool f32, hipStream_t s) {
-  DecodeParams p = params;
-  hipError_t e;
+hipError_t launch_decode_pieces(DecodeParams& p, bool f32, hipStream_t s) {
   if (p.fp6 && (f32 || !mfma_supported(p))) return hipErrorNotSupported;  // matrix-core kernel only
   if (f32) {  // debug mode: fp32 everywhere, fp32 pieces
     p.partial_bf16 = 0;
     p.seq_units = nullptr;
-    e = launch_valu<float>(p, s);
-    if (e == hipSuccess) e = launch_merge<float, false>(p, s);
-  } else if (mfma_supported(p)) {  // the matrix-core kernel writes normalised bf16 pieces
-    p.partial_bf16 = 1;
-    e = launch_decode_mfma(p, s);
-    if (e == hipSuccess) {
-      if (p.num_units >= 16 * p.batch) {  // long sequences: many pieces each
-        hipLaunchKernelGGL(merge_pieces_kernel<uint16_t>, dim3(p.batch, p.heads), dim3(256), 0, s, p);
-        e = hipGetLastError();
-      } else {
-        e = launch_merge<uint16_t, true>(p, s);
-      }
-    }
-  } else {
-    p.partial_bf16 = 0;
-    p.seq_units = nullptr;
-    e = launch_valu<uint16_t>(p, s);
-    if (e == hipSuccess) e = launch_merge<uint16_t, false>(p, s);
+    return launch_valu<float>(p, s);
   }
-  return e;
+  if (mfma_supported(p)) {  // the matrix-core kernel writes normalised bf16 pieces
+    p.partial_bf16 = 1;
+    return launch_decode_mfma(p, s);
+  }
+  p.partial_bf16 = 0;
+  p.seq_units = nullptr;
+  return launch_valu<uint16_t>(p, s);
+}
+
+hipError_t launch_decode(const DecodeParams& params, bool f32, hipStream_t s) {
+  DecodeParams p = params;
+  hipError_t e = launch_decode_pieces(p, f32, s);
+  if (e != hipSuccess) return e;
+  if (f32) return launch_merge<float, false>(p, s);
+  if (!p.partial_bf16) return launch_merge<uint16_t, false>(p, s);
+  if (p.num_units >= 16 * p.batch) {  // long sequences: many pieces each
+    hipLaunchKernelGGL(merge_pieces_kernel<uint16_t>, dim3(p.batch, p.heads), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+  return launch_merge<uint16_t, true>(p, s);
 }
 
 }  // namespace mla

@@ -205,6 +205,74 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
                        false, stream);
 }
 
+// Paths that merge into o_lat before projecting (the fp32 debug mode, and bf16 at 16 heads where the
+// vector-ALU decode leaves fp32 pieces) keep o_lat behind the decode's workspace when the caller
+// passes none: room for it in fp32.
+static size_t decode_out_proj_extra(int batch, int num_heads, mla_dtype) {
+  return (size_t)batch * num_heads * kDc * sizeof(float);
+}
+
+size_t mla_decode_out_proj_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
+                                          mla_dtype dtype) {
+  const size_t base = mla_decode_workspace_size(batch, num_heads, max_blocks_per_seq, num_splits, dtype);
+  return base ? base + decode_out_proj_extra(batch, num_heads, dtype) : 0;
+}
+
+mla_status mla_decode_out_proj(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                               const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                               int batch, int num_heads, float softmax_scale, const void* w_uv, void* out,
+                               void* o_lat, float* lse, void* workspace, size_t workspace_bytes_given,
+                               int num_splits, mla_dtype dtype, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (!valid_heads(num_heads)) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1 || num_splits < 0) return MLA_ERR_SHAPE;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q_abs || !kv_cache || !block_table || !seq_lens || !w_uv || !out) return MLA_ERR_NULL;
+  const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq);
+  const size_t base = workspace_bytes(batch, num_heads, units);
+  if (!workspace || workspace_bytes_given < base + decode_out_proj_extra(batch, num_heads, dtype))
+    return MLA_ERR_WORKSPACE;
+  if (debug_checks_enabled()) {
+    bool bad = false;
+    if (check_tables(block_table, max_blocks_per_seq, seq_lens, batch, num_pages, false, stream, &bad) != hipSuccess)
+      return MLA_ERR_HIP;
+    if (bad) return MLA_ERR_BLOCK_TABLE;
+  }
+  DecodeParams p;
+  p.q_abs = q_abs;
+  p.cache = static_cast<const uint16_t*>(kv_cache);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.o_lat = o_lat;
+  p.lse = lse;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + ((size_t)units + batch) * num_heads * kDc;
+  p.seq_units = reinterpret_cast<int*>(p.ws_ml + ((size_t)units + batch) * num_heads * 2);
+  p.fp6 = 0;
+  p.positions = nullptr;
+  p.pos_stride = 0;
+  p.num_pages = num_pages;
+  p.max_blocks = max_blocks_per_seq;
+  p.batch = batch;
+  p.heads = num_heads;
+  p.num_units = units;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.partial_bf16 = 0;
+  hipError_t e;
+  const bool f32 = dtype == MLA_F32;
+  if (f32 || !mfma_supported(p) || !merge_out_proj_supported(p)) {  // the two calls in turn
+    if (!p.o_lat) p.o_lat = static_cast<char*>(workspace) + base;
+    e = launch_decode(p, f32, stream);
+    if (e == hipSuccess) e = launch_out_proj(p.o_lat, w_uv, out, batch, num_heads, f32, stream);
+  } else {  // the matrix-core decode's bf16 pieces, merged and projected in one kernel
+    e = launch_decode_pieces(p, false, stream);
+    if (e == hipSuccess) e = launch_merge_out_proj(p, w_uv, out, stream);
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 size_t mla_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
 mla_status mla_decode_noalloc(const void* q_abs, const void* kv_cache, int num_pages, int page_size,

@@ -162,4 +162,36 @@ struct SegmentWalker {
   }
 };
 
+// Units that hold sequence b: [wf, wl], from the table the matrix-core kernel writes, else derived
+// from seq_lens.  A unit in that range holds no page (and wrote nothing) only when there are more
+// units than pages.
+struct SeqUnits {
+  int wf, wl, W;
+  bool all_live;
+  long long P;
+  __device__ __forceinline__ bool live(int w) const {
+    return all_live || unit_start(P, W, w) != unit_start(P, W, w + 1);
+  }
+};
+
+__device__ __forceinline__ SeqUnits seq_units_of(const DecodeParams& p, int b, long long np) {
+  SeqUnits u;
+  u.W = p.num_units;
+  u.P = 0;
+  if (p.seq_units) {
+    const int4 d = *reinterpret_cast<const int4*>(p.seq_units + 4 * b);
+    u.wf = d.x;
+    u.wl = d.y;
+    u.all_live = d.z != 0;
+    if (!u.all_live) u.P = total_pages(p.seq_lens, p.batch);
+  } else {
+    u.P = total_pages(p.seq_lens, p.batch);
+    const long long before = pages_before(p.seq_lens, b);
+    u.wf = unit_of_page(u.P, u.W, before);
+    u.wl = unit_of_page(u.P, u.W, before + np - 1);
+    u.all_live = u.P >= u.W;
+  }
+  return u;
+}
+
 }  // namespace mla

@@ -61,6 +61,15 @@ hipError_t launch_absorb(const void* q, const void* w_uk, void* q_abs, int batch
 hipError_t launch_out_proj(const void* o_lat, const void* w_uv, void* out, int batch, int heads,
                            bool f32, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, bool f32, hipStream_t s);
+// The bf16 matrix-core decode handles these sizes (the rest run on the vector-ALU kernel).
+bool mfma_supported(const DecodeParams& p);
+// The decode kernel alone: leaves each piece in the workspace (p.partial_bf16 and p.seq_units set
+// to what the kernel wrote) for a merge to finish.
+hipError_t launch_decode_pieces(DecodeParams& p, bool f32, hipStream_t s);
+// Merge of the pieces and the W_UV projection in one kernel (bf16): out [B][H][128], o_lat and lse
+// written when non-null.  Heads must be a multiple of 8.
+hipError_t launch_merge_out_proj(const DecodeParams& p, const void* w_uv, void* out, hipStream_t s);
+bool merge_out_proj_supported(const DecodeParams& p);
 // Producer side: rows [h W_DKV | RoPE(h W_KR)] written at positions[b]; part is the fp32 workspace
 // of append_hidden_workspace_bytes(batch).
 hipError_t launch_append_hidden(void* cache, const int32_t* block_table, int max_blocks,

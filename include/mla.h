@@ -156,6 +156,27 @@ mla_status mla_decode(const void* q_abs, const void* kv_cache, int num_pages, in
                       hipStream_t stream);
 
 /*
+ * mla_decode and mla_out_proj in one call (explainer Step 6: the values are never built per token;
+ * W_UV is applied once, after the weighted sum of the latent notes):
+ *   out[b][h] = o_lat[b][h] @ W_UV[h],  o_lat as mla_decode computes it.
+ * The split merge and the projection run as one kernel (bf16), so o_lat need not go through
+ * memory: o_lat [batch][heads][512] and lse [batch][heads] are written only when non-null.  out
+ * [batch][heads][128], w_uv [heads][512][128]; element types as for mla_decode / mla_out_proj (fp32
+ * for MLA_F32, where the two run one after the other, as they do in bf16 at 16 heads).  In bf16, o_lat is rounded to bf16 before
+ * the projection, as when it passes through memory between the two calls; results agree with
+ * mla_decode followed by mla_out_proj within rounding.  workspace: at least
+ * mla_decode_out_proj_workspace_size(...) bytes, contents on entry ignored.  Errors as mla_decode,
+ * plus MLA_ERR_NULL for a null w_uv or out.
+ */
+size_t mla_decode_out_proj_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
+                                          mla_dtype dtype);
+mla_status mla_decode_out_proj(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
+                               const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                               int batch, int num_heads, float softmax_scale, const void* w_uv, void* out,
+                               void* o_lat, float* lse, void* workspace, size_t workspace_bytes,
+                               int num_splits, mla_dtype dtype, hipStream_t stream);
+
+/*
  * mla_decode without a workspace, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments, results and
  * errors are those of mla_decode, minus workspace and workspace_bytes: the scratch space comes from

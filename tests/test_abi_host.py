@@ -284,3 +284,27 @@ def test_decode_noalloc_validation():
     assert call(batch=-1) == -2
     assert call(q=None) == -1
     assert call(batch=0) == 0
+
+
+def test_decode_out_proj_validation_and_workspace():
+    L = _lib()
+    base = L.mla_decode_workspace_size(4, 128, 64, 0)
+    # room for an fp32 o_lat behind the decode's workspace, for the paths that keep it
+    assert L.mla_decode_out_proj_workspace_size(4, 128, 64, 0) == base + 4 * 128 * 512 * 4
+    assert L.mla_decode_out_proj_workspace_size(4, 128, 64, 0, 1) == \
+        L.mla_decode_workspace_size(4, 128, 64, 0, 1) + 4 * 128 * 512 * 4
+    assert L.mla_decode_out_proj_workspace_size(4, 100, 64, 0) == 0
+
+    def call(batch=1, heads=128, w_uv=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30, page_size=64, dtype=0):
+        return L.lib.mla_decode_out_proj(FAKE, FAKE, 16, page_size, FAKE, 16, FAKE, batch, heads, 0.07, w_uv, out,
+                                         None, None, ws, ws_bytes, 0, dtype, None)
+
+    assert call(w_uv=None) == -1
+    assert call(out=None) == -1
+    assert call(ws=None) == -4
+    assert call(ws_bytes=16) == -4
+    assert call(page_size=32) == -5
+    assert call(heads=100) == -5
+    assert call(dtype=5) == -3
+    assert call(batch=-2) == -2
+    assert call(batch=0) == 0
