@@ -263,8 +263,7 @@ def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_
     comp = torch.empty((B * pk, 64, ROW_ELEMS), dtype=torch.bfloat16, device=dev)
     comp_bt = torch.empty((B, pk), dtype=torch.int32, device=dev)
     ws_d = torch.empty(lib.mla_decode_workspace_size(B, H, pk, 0), dtype=torch.uint8, device=dev)
-    inplace = H >= 32                  # the in-place decode runs on the matrix-core kernel only
-    ws_i = torch.empty(lib.mla_decode_topk_workspace_size(B, H, k) if inplace else 0, dtype=torch.uint8, device=dev)
+    ws_i = torch.empty(lib.mla_decode_topk_workspace_size(B, H, k), dtype=torch.uint8, device=dev)
     o_g = torch.empty(B, H, D_C, dtype=torch.bfloat16, device=dev)
     o_i = torch.empty(B, H, D_C, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(B, H, dtype=torch.float32, device=dev)
@@ -279,8 +278,7 @@ def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_
         if marks: marks[2].record(stream)
         lib.mla_decode(q_abs, comp, comp_bt, cnt, wl.scale, o_g, lse, ws_d)
         if marks: marks[3].record(stream)
-        if inplace:
-            lib.mla_decode_topk(q_abs, cache, bt, pos, cnt, wl.scale, o_i, lse, ws_i)
+        lib.mla_decode_topk(q_abs, cache, bt, pos, cnt, wl.scale, o_i, lse, ws_i)
         if marks:
             marks[4].record(stream)
             ev.append(marks)
@@ -291,18 +289,17 @@ def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_
     for _ in range(steps):
         run(ev)
     torch.cuda.synchronize()
-    if inplace and not torch.equal(o_g.view(torch.int16), o_i.view(torch.int16)):
+    if not torch.equal(o_g.view(torch.int16), o_i.view(torch.int16)):
         raise SystemExit("mla_decode_topk differs from mla_gather_rows + mla_decode")
     st = [sum(m[i].elapsed_time(m[i + 1]) for m in ev) / len(ev) for i in range(4)]
     ms_gather_path = st[0] + st[1] + st[2]
-    ms = st[0] + st[3] if inplace else ms_gather_path
+    ms = st[0] + st[3]
     kept = int(cnt.sum().item())
     nbytes = wl.tokens * 128 + kept * ROW_BYTES
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"calls": "mla_index_topk + mla_decode_topk" if inplace else
-            f"mla_index_topk + mla_gather_rows + mla_decode (no in-place decode at {H} heads)",
+    return {"calls": "mla_index_topk + mla_decode_topk",
             "k": k, "kept_tokens": kept, "scored_tokens": wl.tokens, "ms_per_call": round(ms, 5),
-            "ms_topk": round(st[0], 5), "ms_decode_topk": round(st[3], 5) if inplace else None,
+            "ms_topk": round(st[0], 5), "ms_decode_topk": round(st[3], 5),
             "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "dense_decode_ms": round(dense_ms, 5),
             "speedup_vs_dense": round(dense_ms / ms, 3),

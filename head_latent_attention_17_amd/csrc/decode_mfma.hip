@@ -559,9 +559,13 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   // The query of a segment lives in VGPRs for the whole segment (36 x 8 bf16 per lane).
   const uint16_t* qa = static_cast<const uint16_t*>(p.q_abs);
   bf16x8 q[36];
+  // Head of accumulator column c (0 .. 31) of this wave.  With 16 heads the columns 16 .. 31 repeat
+  // heads 0 .. 15: same query, same data, so bit-identical results, and every store they make
+  // writes the same bits to the same place as the real head's.  (Heads are powers of two.)
+  auto head_of = [&](int c) __attribute__((always_inline)) { return (wave * 32 + c) & (p.heads - 1); };
   auto load_q = [&](int b) __attribute__((always_inline)) {
     const int ln = lane_id();
-    const uint16_t* qrow = qa + ((size_t)b * p.heads + wave * 32 + (ln & 31)) * kRow + 8 * (ln >> 5);
+    const uint16_t* qrow = qa + ((size_t)b * p.heads + head_of(ln & 31)) * kRow + 8 * (ln >> 5);
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
   };
@@ -857,7 +861,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         // final write overwrites anyway, so scaling them never holds more than one block in VGPRs.
         mfma_a_drain(o);
         const int ln = lane_id();
-        float* slot = p.ws_o + (((size_t)w + b) * p.heads + wave * 32 + (ln & 31)) * kDc + 4 * (ln >> 5);
+        float* slot = p.ws_o + (((size_t)w + b) * p.heads + head_of(ln & 31)) * kDc + 4 * (ln >> 5);
 #pragma unroll
         for (int db = 0; db < 16; ++db) {
 #pragma unroll
@@ -882,9 +886,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         }
         // Q is read again from memory: redefining it here frees its 144 VGPRs for this block
         // instead of leaving the register allocator to spill it around the hot loop.
-        const uint16_t* qrow = qa + ((size_t)b * p.heads + wave * 32 + (ln & 31)) * kRow + 8 * (ln >> 5);
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks) q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+        load_q(b);
         wait_vmcnt<0>();
       }
 
@@ -943,18 +945,19 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     const float inv = 1.f / l_tot;
     mfma_a_drain(o);
     const int ln = lane_id();
-    const size_t part = ((size_t)w + b) * p.heads + wave * 32 + (ln & 31);
+    const size_t part = ((size_t)w + b) * p.heads + head_of(ln & 31);
     // four sums of one lane, divided by the softmax sum, rounded to bf16 (nearest even)
     auto packed_out = [&](int db, int g) __attribute__((always_inline)) {
       const bf16x4 v = {(__bf16)(o[db][4 * g] * inv), (__bf16)(o[db][4 * g + 1] * inv),
                         (__bf16)(o[db][4 * g + 2] * inv), (__bf16)(o[db][4 * g + 3] * inv)};
       return __builtin_bit_cast(u32x2, v);
     };
-    if constexpr (NW == 4) {
-      // Rows go through LDS and leave as 256-byte quarter rows instead of 16-byte pieces of 32
-      // rows per store.  Once every wave is done with the last tile its stage is free: each wave
-      // takes a quarter of it, 32 heads x 128 dims padded by 16 bytes per row against bank
-      // conflicts, and passes its rows through it a quarter at a time.
+    {
+      // Rows go through LDS and leave as 256-byte quarter rows: written straight from the
+      // accumulator layout, each store would write 8-byte pieces of 32 rows (about 20,000 cycles
+      // for a unit's stores instead of about 6,500).  Once every wave is done with the last tile
+      // its stage is free: each wave takes 32 heads x 128 dims of it, padded by 16 bytes per row
+      // against bank conflicts, and passes its rows through a quarter at a time.
       constexpr int kPad = 256 + 16;
       __builtin_amdgcn_s_barrier();
       LDS_AS char* region = (LDS_AS char*)ring[stg(it - 1)] + wave * 32 * kPad;
@@ -971,16 +974,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         for (int k = 0; k < 8; ++k) {
           const int h = 4 * k + (ln >> 4);
           const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(region + h * kPad + (ln & 15) * 16);
-          const size_t ph = ((size_t)w + b) * p.heads + wave * 32 + h;
+          const size_t ph = ((size_t)w + b) * p.heads + head_of(h);
           *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.ws_o + ph * kDc) + 128 * qt + 8 * (ln & 15)) = v;
         }
-      }
-    } else {
-      uint16_t* orow = reinterpret_cast<uint16_t*>(p.ws_o + part * kDc) + 4 * (ln >> 5);
-#pragma unroll
-      for (int db = 0; db < 16; ++db) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g) = packed_out(db, g);
       }
     }
     if (ln < 32) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_ref, l_tot);
@@ -991,7 +987,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
 
 }  // namespace
 
-bool mfma_supported(const DecodeParams& p) { return p.heads == 128 || p.heads == 64 || p.heads == 32; }
+bool mfma_supported(const DecodeParams& p) {
+  return p.heads == 128 || p.heads == 64 || p.heads == 32 || p.heads == 16;
+}
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
   if (p.fp6) {
@@ -1009,7 +1007,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
     switch (p.heads) {
       case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false, true>), dim3(p.num_units), dim3(256), 0, s, p); break;
       case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false, true>), dim3(p.num_units), dim3(128), 0, s, p); break;
-      case 32: hipLaunchKernelGGL((decode_mfma_kernel<1, false, true>), dim3(p.num_units), dim3(64), 0, s, p); break;
+      case 32:
+      case 16: hipLaunchKernelGGL((decode_mfma_kernel<1, false, true>), dim3(p.num_units), dim3(64), 0, s, p); break;
       default: return hipErrorNotSupported;
     }
     return hipGetLastError();
@@ -1017,7 +1016,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
   switch (p.heads) {
     case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false, false>), dim3(p.num_units), dim3(256), 0, s, p); break;
     case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false, false>), dim3(p.num_units), dim3(128), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<1, false, false>), dim3(p.num_units), dim3(64), 0, s, p); break;
+    case 32:
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<1, false, false>), dim3(p.num_units), dim3(64), 0, s, p); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

@@ -10,10 +10,12 @@
 
 namespace mla {
 
-int auto_units(int batch, int heads, int max_blocks) {
-  // Enough page ranges to give every compute unit work, but never more ranges than pages.
+int auto_units(int batch, int heads, int max_blocks, bool f32) {
+  // Enough page ranges to give every compute unit work, but never more ranges than pages.  The
+  // matrix-core kernel (bf16) runs one workgroup per compute unit; the fp32 debug kernel splits each
+  // range further by 8-head groups, so at 16 heads it takes twice the ranges.
   const long long pages_bound = (long long)batch * (long long)max_blocks;
-  long long units = (heads >= 32) ? kNumCUs : 2 * kNumCUs;
+  long long units = (f32 && heads < 32) ? 2 * kNumCUs : kNumCUs;
   if (units > pages_bound) units = pages_bound;
   if (units < 1) units = 1;
   return (int)units;
@@ -51,7 +53,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: invalid or inconsistent size";
     case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown dtype";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
-    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: page_size must be 64, heads in {16,32,64,128} (64 or 128 and bf16 for the ~6-bit cache, 32 to 128 for mla_decode_topk)";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: page_size must be 64, heads in {16,32,64,128} (64 or 128 and bf16 for the ~6-bit cache)";
     case MLA_ERR_BLOCK_TABLE: return "MLA_ERR_BLOCK_TABLE: block table entry out of range";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch failed";
     case MLA_ERR_SCRATCH: return "MLA_ERR_SCRATCH: these sizes need more scratch than mla_decode_noalloc's fixed device buffer holds";
@@ -66,7 +68,7 @@ size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_se
   if (batch < 0 || max_blocks_per_seq < 1 || num_splits < 0 || !valid_heads(num_heads) ||
       !valid_dtype(dtype))
     return 0;
-  const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq);
+  const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq, dtype == MLA_F32);
   return workspace_bytes(batch, num_heads, units);
 }
 
@@ -156,7 +158,7 @@ static mla_status decode_common(const void* q_abs, const void* kv_cache, int num
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!q_abs || !kv_cache || !block_table || !seq_lens || !o_lat) return MLA_ERR_NULL;
-  const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq);
+  const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq, dtype == MLA_F32);
   const size_t need = workspace_bytes(batch, num_heads, units);
   if (noalloc) {
     if (need > kNoAllocScratchBytes) return MLA_ERR_SCRATCH;
@@ -230,7 +232,7 @@ mla_status mla_decode_out_proj(const void* q_abs, const void* kv_cache, int num_
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!q_abs || !kv_cache || !block_table || !seq_lens || !w_uv || !out) return MLA_ERR_NULL;
-  const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq);
+  const int units = num_splits ? num_splits : auto_units(batch, num_heads, max_blocks_per_seq, dtype == MLA_F32);
   const size_t base = workspace_bytes(batch, num_heads, units);
   if (!workspace || workspace_bytes_given < base + decode_out_proj_extra(batch, num_heads, dtype))
     return MLA_ERR_WORKSPACE;
@@ -392,7 +394,7 @@ mla_status mla_gather_rows(const void* kv_cache, int num_pages, int page_size, c
 size_t mla_decode_topk_workspace_size(int batch, int num_heads, int k) {
   if (batch < 0 || k < 1 || !valid_heads(num_heads)) return 0;
   const int kept_pages = (int)(((long long)k + kPage - 1) / kPage);
-  return workspace_bytes(batch, num_heads, auto_units(batch, num_heads, kept_pages));
+  return workspace_bytes(batch, num_heads, auto_units(batch, num_heads, kept_pages, false));
 }
 
 mla_status mla_decode_topk(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
@@ -404,12 +406,11 @@ mla_status mla_decode_topk(const void* q_abs, const void* kv_cache, int num_page
   if (!valid_heads(num_heads)) return MLA_ERR_UNSUPPORTED;
   if (batch < 0 || num_pages < 0 || max_blocks_per_seq < 1 || k < 1) return MLA_ERR_SHAPE;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return MLA_ERR_SHAPE;
-  if (num_heads < 32) return MLA_ERR_UNSUPPORTED;  // matrix-core kernel only
   if (batch == 0) return MLA_OK;
   if (num_pages < 1) return MLA_ERR_SHAPE;
   if (!q_abs || !kv_cache || !block_table || !positions || !counts || !o_lat) return MLA_ERR_NULL;
   const int kept_pages = (int)(((long long)k + kPage - 1) / kPage);
-  const int units = auto_units(batch, num_heads, kept_pages);
+  const int units = auto_units(batch, num_heads, kept_pages, false);
   const size_t need = workspace_bytes(batch, num_heads, units);
   if (!workspace || workspace_bytes_given < need) return MLA_ERR_WORKSPACE;
   if (debug_checks_enabled()) {

@@ -49,7 +49,7 @@ struct DecodeParams {
   float scale_log2;    // softmax_scale * log2(e)
 };
 
-int auto_units(int batch, int heads, int max_blocks);
+int auto_units(int batch, int heads, int max_blocks, bool f32);
 size_t workspace_bytes(int batch, int heads, int units);
 
 // Launchers: return hipSuccess or the launch error.

@@ -298,12 +298,12 @@ mla_status mla_gather_rows(const void* kv_cache, int num_pages, int page_size, c
  * attends to the tokens at positions[b][0 .. counts[b]) (positions [batch][k] and counts [batch]
  * as mla_index_topk writes them; any token positions in list order are allowed), each row read
  * through block_table as mla_decode reads it.  counts[b] = 0 gives o_lat = 0 and lse = -inf.
- * q_abs, o_lat, lse and scale as for mla_decode; bf16 only; num_heads in {32, 64, 128}.
+ * q_abs, o_lat, lse and scale as for mla_decode; bf16 only; num_heads in {16, 32, 64, 128}.
  * workspace: at least mla_decode_topk_workspace_size(batch, num_heads, k) bytes, contents
  * irrelevant, used only during the call.  Counts and positions are trusted on the fast path; with
  * MLA_DEBUG_CHECKS=1 a count above k, a position outside the table row or a table entry outside
  * [0, num_pages) returns MLA_ERR_BLOCK_TABLE, launching nothing else.
- * Errors: MLA_ERR_UNSUPPORTED (page_size != 64, num_heads not in {32, 64, 128}), MLA_ERR_SHAPE (k < 1,
+ * Errors: MLA_ERR_UNSUPPORTED (page_size != 64, num_heads not in {16, 32, 64, 128}), MLA_ERR_SHAPE (k < 1,
  * negative sizes, num_pages < 1 with batch > 0, scale not finite and positive), MLA_ERR_NULL,
  * MLA_ERR_WORKSPACE, MLA_ERR_HIP.
  */

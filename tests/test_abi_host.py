@@ -234,7 +234,7 @@ def test_decode_topk_validation():
     """In-place top-k decode: its workspace is that of mla_decode over compact pages of the kept
     rows (ceil(k / 64) pages per sequence), and host validation runs before any launch."""
     L = _lib()
-    for b, h, k in ((4, 128, 2048), (32, 128, 2048), (3, 64, 100), (1, 32, 1)):
+    for b, h, k in ((4, 128, 2048), (32, 128, 2048), (3, 64, 100), (1, 32, 1), (2, 16, 300)):
         assert L.mla_decode_topk_workspace_size(b, h, k) == L.mla_decode_workspace_size(b, h, -(-k // 64), 0)
     assert L.mla_decode_topk_workspace_size(4, 128, 0) == 0
     assert L.mla_decode_topk_workspace_size(4, 48, 64) == 0
@@ -246,7 +246,6 @@ def test_decode_topk_validation():
         a[i] = v
         return f(*a)
     assert call(3, 32) == -5                       # page size
-    assert call(10, 16) == -5                      # no matrix-core kernel for 16 heads
     assert call(10, 48) == -5
     assert call(9, 0) == -2                        # k
     assert call(8, -1) == -2                       # batch

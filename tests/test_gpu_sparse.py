@@ -185,7 +185,7 @@ def _oracle_list_decode(hi, wl, pos, cnt, seqs, heads):
     return o, lse
 
 
-@pytest.mark.parametrize("heads,k", [(128, 100), (128, 256), (64, 7), (64, 100), (32, 256)])
+@pytest.mark.parametrize("heads,k", [(128, 100), (128, 256), (64, 7), (64, 100), (32, 256), (16, 100)])
 def test_decode_topk_matches_gather(lib, heads, k):
     """mla_decode_topk over mla_index_topk's lists equals mla_gather_rows + mla_decode bit for bit
     (empty, short, ragged and long sequences), and the oracle within the bf16 tolerance."""
