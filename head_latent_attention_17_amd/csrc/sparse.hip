@@ -13,6 +13,9 @@
 //   write     per chunk, keys above T and equal to T are counted; each chunk's output offset is
 //             the kept count of the chunks before it (two sums, since equal keys are kept in
 //             position order), and each chunk writes its kept positions, in increasing order.
+//   short     with at most 16,384 tokens per block table, scoring is followed by one workgroup
+//             per sequence that does both passes and the write in LDS (two launches, and no
+//             global histogram to clear).
 //   gather    copies the kept rows into compact pages (sequence b owns pages b P .. b P + P - 1,
 //             P = ceil(k / 64)) and writes their block table, so that mla_decode runs over them
 //             unchanged.  mla_decode_topk reads the same rows in place instead (the decode
@@ -26,6 +29,8 @@ constexpr int kIndexDim = 128;
 constexpr int kChunk = 1024;          // positions per workgroup in the selection passes (and scoring)
 constexpr int kBins1 = 4096;          // key >> 11: keys are score + 2^21, in [0, 2^22]
 constexpr int kBins2 = 2048;          // key & 2047
+constexpr int kSmallMax = 16384;      // block tables up to this many tokens: one workgroup per sequence
+constexpr int kSmallThreads = 1024;
 
 // Workspace layout (int32), per sequence b:
 //   scores [B][stride]; hist1 [B][4096]; hist2 [B][2048]; pick [B][4] (hi bin, left after it,
@@ -52,7 +57,7 @@ __global__ __launch_bounds__(256) void topk_clear_kernel(TopkWs w) {
 // plus the histogram of their high key bits, gathered in LDS and added to the sequence's histogram.
 // CH (a multiple of 256, at most the selection chunk) is smaller when the batch has few chunks, so
 // that the grid still fills the compute units.
-template <int CH>
+template <int CH, bool HIST>
 __global__ __launch_bounds__(256) void index_score_kernel(const int8_t* __restrict__ index_cache,
                                                           const int32_t* __restrict__ block_table, int max_blocks,
                                                           const int32_t* __restrict__ seq_lens,
@@ -63,8 +68,10 @@ __global__ __launch_bounds__(256) void index_score_kernel(const int8_t* __restri
   const int len = seq_lens[b];
   const int t0 = blockIdx.x * CH;
   if (t0 >= len) return;
-  for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0;
-  __syncthreads();
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0;
+    __syncthreads();
+  }
   const int part = threadIdx.x & 7;  // 16-byte part of the vector
   const int4 q = *reinterpret_cast<const int4*>(q_index + (size_t)b * kIndexDim + 16 * part);
   int32_t* __restrict__ scores = w.scores + (size_t)b * w.stride;
@@ -97,13 +104,15 @@ __global__ __launch_bounds__(256) void index_score_kernel(const int8_t* __restri
       sc += __shfl_xor(sc, 4, 64);
       if (t < len && part == 0) {
         scores[t] = sc;
-        atomicAdd(&hist[key_of(sc) >> 11], 1);
+        if constexpr (HIST) atomicAdd(&hist[key_of(sc) >> 11], 1);
       }
     }
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kBins1; i += 256)
-    if (hist[i]) atomicAdd(&w.hist1[(size_t)b * kBins1 + i], hist[i]);
+  if constexpr (HIST) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kBins1; i += 256)
+      if (hist[i]) atomicAdd(&w.hist1[(size_t)b * kBins1 + i], hist[i]);
+  }
 }
 
 // Inclusive scan over a workgroup of NT threads (one value each) through the wave totals in LDS;
@@ -134,18 +143,19 @@ __device__ __forceinline__ int block_scan(int v, int* wsum, int* total) {
 }
 
 // Finds, from the top, the bin where the running count reaches `need` (pass 1: need = k; pass 2:
-// what pass 1 left).  256 threads, thread i owns bins [i NB / 256, (i + 1) NB / 256).
-template <int NB>
+// what pass 1 left).  NT threads, thread i owns bins [i NB / NT, (i + 1) NB / NT) counted from the
+// top; exactly one thread writes the result.
+template <int NB, int NT = 256>
 __device__ __forceinline__ void pick_bin(const int32_t* hist, int need, int* out_bin, int* out_left) {
-  __shared__ int wsum[4];
+  __shared__ int wsum[NT / 64];
   __shared__ int tot;
-  constexpr int per = NB / 256;
+  constexpr int per = NB / NT;
   const int i = threadIdx.x;
-  // thread i takes bins counted from the top: (255 - i) per .. + per - 1, scanned top first
+  // thread i takes bins counted from the top: (NT - 1 - i) per .. + per - 1, scanned top first
   const int hi_bin = NB - 1 - i * per;
   int mine = 0;
   for (int j = 0; j < per; ++j) mine += hist[hi_bin - j];
-  const int incl = block_scan<256>(mine, wsum, &tot);
+  const int incl = block_scan<NT>(mine, wsum, &tot);
   const int before = incl - mine;  // keys in the bins above this thread's range
   if (before < need && incl >= need) {
     int cum = before, d = hi_bin;
@@ -264,6 +274,84 @@ __global__ __launch_bounds__(kChunk) void topk_write_kernel(const int32_t* __res
   if (take) positions[(size_t)b * k + at] = t;
 }
 
+// The selection for one sequence in one workgroup, for block tables of at most kSmallMax tokens:
+// its scores (written by the scoring kernel) are staged in LDS, both radix passes count in LDS, and
+// the kept positions are written in increasing order (each thread owns a run of consecutive
+// positions; two scans place the runs).  Same result as the multi-workgroup passes: the k highest keys, ties to the earlier
+// position.
+__global__ __launch_bounds__(kSmallThreads) void topk_select_small_kernel(const int32_t* __restrict__ seq_lens,
+                                                                         int k, TopkWs w,
+                                                                         int32_t* __restrict__ positions,
+                                                                         int32_t* __restrict__ counts) {
+  __shared__ int32_t sc[kSmallMax];
+  __shared__ int32_t hist[kBins1];
+  __shared__ int wsum[kSmallThreads / 64];
+  __shared__ int tot[2];
+  __shared__ int d_s, left_s;
+  const int b = blockIdx.x;
+  const int len = max(seq_lens[b], 0);
+  const int tid = threadIdx.x;
+  if (tid == 0) counts[b] = min(len, k);
+  int32_t* out = positions + (size_t)b * k;
+  if (len <= k) {  // every token is kept
+    for (int t = tid; t < len; t += kSmallThreads) out[t] = t;
+    return;
+  }
+  for (int i = tid; i < kBins1; i += kSmallThreads) hist[i] = 0;
+  __syncthreads();
+  {
+    const int32_t* src = w.scores + (size_t)b * w.stride;
+    int v[kSmallMax / kSmallThreads];
+#pragma unroll
+    for (int u = 0; u < kSmallMax / kSmallThreads; ++u) {
+      const int t = tid + u * kSmallThreads;
+      v[u] = t < len ? src[t] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kSmallMax / kSmallThreads; ++u) {
+      const int t = tid + u * kSmallThreads;
+      if (t < len) {
+        sc[t] = v[u];
+        atomicAdd(&hist[key_of(v[u]) >> 11], 1);
+      }
+    }
+  }
+  __syncthreads();
+  pick_bin<kBins1, kSmallThreads>(hist, k, &d_s, &left_s);
+  __syncthreads();
+  const int d1 = d_s, left1 = left_s;
+  for (int i = tid; i < kBins2; i += kSmallThreads) hist[i] = 0;
+  __syncthreads();
+  for (int t = tid; t < len; t += kSmallThreads) {
+    const int key = key_of(sc[t]);
+    if ((key >> 11) == d1) atomicAdd(&hist[key & 2047], 1);
+  }
+  __syncthreads();
+  pick_bin<kBins2, kSmallThreads>(hist, left1, &d_s, &left_s);
+  __syncthreads();
+  const int T = (d1 << 11) | d_s, need_eq = left_s;
+  // Thread i owns the J consecutive positions from J i: one scan of the keys equal to T (those kept
+  // are the first need_eq of them), one of the kept positions, then each thread writes its own.
+  const int J = (len + kSmallThreads - 1) / kSmallThreads;
+  const int t0 = tid * J, t1 = min(t0 + J, len);
+  int eq_mine = 0;
+  for (int t = t0; t < t1; ++t) eq_mine += key_of(sc[t]) == T;
+  int eq_rank = block_scan<kSmallThreads>(eq_mine, wsum, &tot[0]) - eq_mine;
+  int take_mine = 0;
+  for (int t = t0; t < t1; ++t) {
+    const int key = key_of(sc[t]);
+    take_mine += key > T || (key == T && eq_rank < need_eq);
+    eq_rank += key == T;
+  }
+  int at = block_scan<kSmallThreads>(take_mine, wsum, &tot[1]) - take_mine;
+  eq_rank -= eq_mine;
+  for (int t = t0; t < t1; ++t) {
+    const int key = key_of(sc[t]);
+    if (key > T || (key == T && eq_rank < need_eq)) out[at++] = t;
+    eq_rank += key == T;
+  }
+}
+
 // Row i < counts[b] of sequence b: 72 lanes of 16 bytes from its page to compact page
 // b * P + i / 64, slot i % 64.  The first row's workgroup also writes the compact block table.
 __global__ __launch_bounds__(128) void gather_rows_kernel(const uint16_t* __restrict__ cache,
@@ -313,18 +401,31 @@ hipError_t launch_index_topk(const int8_t* index_cache, const int32_t* block_tab
                              int32_t* counts, void* workspace, hipStream_t s) {
   const TopkWs w = topk_ws(workspace, batch, max_blocks);
   const dim3 chunks(w.nchunks, batch);
-  hipLaunchKernelGGL(topk_clear_kernel, dim3(batch), dim3(256), 0, s, w);
   // Scoring chunks: 1,024 tokens, or 256 while that grid would hold fewer than two workgroups per
   // compute unit (32 x 4,096 tokens: 12.0 -> 7.6 us).  Halving the chunks of a 516-workgroup grid
   // (4 x 131,072 tokens) made scoring slower (20.1 -> 22.2 us): more workgroups flush their
   // histograms into the same few hot bins.
-  if ((long long)w.nchunks * batch >= 2 * kNumCUs) {
-    hipLaunchKernelGGL(index_score_kernel<kChunk>, chunks, dim3(256), 0, s, index_cache, block_table, max_blocks,
-                       seq_lens, q_index, w);
-  } else {
-    hipLaunchKernelGGL(index_score_kernel<kChunk / 4>, dim3(4 * w.nchunks, batch), dim3(256), 0, s, index_cache,
-                       block_table, max_blocks, seq_lens, q_index, w);
+  const bool small_chunks = (long long)w.nchunks * batch < 2 * kNumCUs;
+  if ((long long)max_blocks * kPage <= kSmallMax) {
+    // Short block tables: scoring alone, then one workgroup per sequence selects (two launches, no
+    // global histograms to clear).
+    if (small_chunks)
+      hipLaunchKernelGGL((index_score_kernel<kChunk / 4, false>), dim3(4 * w.nchunks, batch), dim3(256), 0, s,
+                         index_cache, block_table, max_blocks, seq_lens, q_index, w);
+    else
+      hipLaunchKernelGGL((index_score_kernel<kChunk, false>), chunks, dim3(256), 0, s, index_cache, block_table,
+                         max_blocks, seq_lens, q_index, w);
+    hipLaunchKernelGGL(topk_select_small_kernel, dim3(batch), dim3(kSmallThreads), 0, s, seq_lens, k, w, positions,
+                       counts);
+    return hipGetLastError();
   }
+  hipLaunchKernelGGL(topk_clear_kernel, dim3(batch), dim3(256), 0, s, w);
+  if (small_chunks)
+    hipLaunchKernelGGL((index_score_kernel<kChunk / 4, true>), dim3(4 * w.nchunks, batch), dim3(256), 0, s,
+                       index_cache, block_table, max_blocks, seq_lens, q_index, w);
+  else
+    hipLaunchKernelGGL((index_score_kernel<kChunk, true>), chunks, dim3(256), 0, s, index_cache, block_table,
+                       max_blocks, seq_lens, q_index, w);
   hipLaunchKernelGGL(topk_hist2_kernel, chunks, dim3(256), 0, s, seq_lens, k, w);
   hipLaunchKernelGGL(topk_count_kernel, chunks, dim3(256), 0, s, seq_lens, w);
   hipLaunchKernelGGL(topk_write_kernel, chunks, dim3(kChunk), 0, s, seq_lens, k, w, positions, counts);

@@ -41,10 +41,17 @@ def _check_positions(wl, idx_np, qi_np, k, pos, cnt, seqs=None):
         assert np.array_equal(pos[b, :len(want)], want), b
 
 
+# block tables of at most 16,384 tokens take the one-launch selection (a workgroup per sequence),
+# longer ones the multi-workgroup passes; both must give the oracle's positions bit for bit
+SHORT = [0, 1, 5, 64, 100, 1000, 5000]
+LONG = [0, 1, 5, 64, 100, 1000, 20000]
+
+
+@pytest.mark.parametrize("lens", [SHORT, LONG], ids=["one_launch", "multi_pass"])
 @pytest.mark.parametrize("k", [1, 7, 64, 256])
-def test_topk_matches_oracle(lib, k):
-    wl = synth.make_custom([0, 1, 5, 64, 100, 1000, 5000], heads=16, seed=140 + k)
-    say("index top-k", k)
+def test_topk_matches_oracle(lib, k, lens):
+    wl = synth.make_custom(lens, heads=16, seed=140 + k)
+    say("index top-k", k, wl.max_blocks * 64)
     idx = synth.index_cache(wl, 0, device="cuda")
     qi = synth.index_queries(wl, 0, device="cuda")
     pos, cnt = _topk(lib, wl, idx, qi, k)
@@ -56,7 +63,8 @@ def test_topk_many_chunks(lib):
     full 1,024-token chunks (the smaller workloads above score in 256-token chunks; the full-size
     test below in 1,024-token chunks over 516 workgroups)."""
     k = 300
-    wl = synth.make_custom([16384 - 7 * i for i in range(64)], heads=16, seed=145)
+    wl = synth.make_custom([16500 - 7 * i for i in range(64)], heads=16, seed=145)
+    assert wl.max_blocks * 64 > 16384
     say("index top-k, 64 x ~16k tokens", k)
     idx = synth.index_cache(wl, 0, device="cuda")
     qi = synth.index_queries(wl, 0, device="cuda")
@@ -64,11 +72,24 @@ def test_topk_many_chunks(lib):
     _check_positions(wl, idx.cpu().numpy(), qi.cpu().numpy(), k, pos, cnt)
 
 
+def test_topk_one_launch_at_capacity(lib):
+    """Sequences filling the one-launch path's LDS (16,384 scores) and just below it."""
+    k = 2048
+    wl = synth.make_custom([16384 - 7 * i for i in range(8)], heads=16, seed=146)
+    assert wl.max_blocks * 64 == 16384
+    say("index top-k at the one-launch capacity", k)
+    idx = synth.index_cache(wl, 0, device="cuda")
+    qi = synth.index_queries(wl, 0, device="cuda")
+    pos, cnt = _topk(lib, wl, idx, qi, k)
+    _check_positions(wl, idx.cpu().numpy(), qi.cpu().numpy(), k, pos, cnt)
+
+
+@pytest.mark.parametrize("lens", [[300, 2000, 64], [300, 20000, 64]], ids=["one_launch", "multi_pass"])
 @pytest.mark.parametrize("levels", [1, 3])
-def test_topk_ties(lib, levels):
+def test_topk_ties(lib, levels, lens):
     """Index vectors with entries in {0} or {-1, 0, 1}: all scores equal, or few distinct values, so
     the tie rule (earlier position first) decides most of the selection."""
-    wl = synth.make_custom([300, 2000, 64], heads=16, seed=150 + levels)
+    wl = synth.make_custom(lens, heads=16, seed=150 + levels)
     say("index top-k ties", levels)
     rng = np.random.default_rng(levels)
     idx_np = (rng.integers(0, levels, (wl.num_pages, 64, 128)) - (levels // 2)).astype(np.int8)
@@ -125,11 +146,12 @@ def test_gathered_rows_and_sparse_decode(lib):
     assert e_o <= BF16_TOL and e_l <= BF16_TOL
 
 
-def test_full_size(lib):
-    """4 x 131,072 tokens (+1), k = 2,048: every sequence's kept positions bit for bit, and the
-    decode over them on sampled heads."""
+@pytest.mark.parametrize("cfg", [3, 2])
+def test_full_size(lib, cfg):
+    """4 x 131,072 tokens (+1) (multi-workgroup passes) and 32 x 4,096 (+1) (one launch), k = 2,048:
+    every sequence's kept positions bit for bit, and the decode over them on sampled heads."""
     import bench
-    wl = bench.bench_workload(3)
+    wl = bench.bench_workload(cfg)
     k = 2048
     say("sparse full size", wl.name)
     g = Gpu(wl)
