@@ -72,8 +72,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
                     help="for counter runs: a few untimed steps, then mla_decode alone, then "
-                         "mla_decode_out_proj, then one 1 GiB device copy that calibrates the byte "
-                         "counters; prints no JSON")
+                         "mla_decode_out_proj, then mla_decode_fp6 over the cache's ~6-bit form, "
+                         "then one 1 GiB device copy that calibrates the byte counters; prints no JSON")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of "
                          "--profile-run into profiles/traffic_<workload>.json; needs no GPU")
@@ -696,13 +696,18 @@ def main():
         for _ in range(args.steps):
             lib.mla_decode_out_proj(res.q_abs, d["cache"], res.bt, res.att, wl.scale, d["w_uv"], res.out, None,
                                     None, res.ws, res.splits)
+        c6 = torch.empty((d["cache"].shape[0], lib.FP6_PAGE_BYTES), dtype=torch.uint8, device=dev)
+        lib.mla_cache_quantize_fp6(d["cache"], c6)
+        for _ in range(args.steps):
+            lib.mla_decode_fp6(res.q_abs, c6, res.bt, res.att, wl.scale, res.o_lat, res.lse, res.ws, res.splits)
         torch.cuda.synchronize()
-        del res
+        del res, c6
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        say(f"profile run done: {args.steps} mla_decode and mla_decode_out_proj calls, one {CALIB_BYTES} B copy")
+        say(f"profile run done: {args.steps} mla_decode, mla_decode_out_proj and mla_decode_fp6 calls, one "
+            f"{CALIB_BYTES} B copy")
         return
 
     main_rec = time_workload(lib, res, args.steps, args.warmup)

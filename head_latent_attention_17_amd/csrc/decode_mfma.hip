@@ -33,16 +33,6 @@
 // With it, the 16 lanes of one row read of the score operand (16 tokens, one chunk) and of one
 // transposing read (4 tokens x 2 chunks) always land on 16 different 16-byte bank groups.
 //
-// ~6-bit cache (FP6 template argument).  Pages hold 6-bit E2M3 codes with one power-of-two scale
-// per row, so every stored number is exactly a bf16 number.  Each wave copies its own rows of a
-// tile (32 / waves rows: codes and scales, 13.6 KB per tile in all) into a wave-private 3-stage
-// LDS ring, four tiles ahead (a stage is free once its tile is converted), and converts them with
-// v_cvt_scalef32_pk32_bf16_fp6 (32 codes per instruction, the scale's exponent applied exactly)
-// into the same swizzled bf16 tile layout, two tiles ahead, spread over the output product.  The bf16 ring then has three stages (the tile whose
-// output product runs, the tile whose scores run, the tile being converted) and everything after it
-// is the bf16 path unchanged.  Reading only the codes, the conversion needs no barrier of its own:
-// a wave converts exactly the rows it copied, and the barrier that opens each iteration publishes
-// the converted tile.
 #include "mla_device.h"
 
 namespace mla {
@@ -56,6 +46,9 @@ typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 typedef __attribute__((__vector_size__(6 * sizeof(unsigned)))) unsigned u32x6;
 typedef __attribute__((__vector_size__(16 * sizeof(unsigned)))) unsigned u32x16;
+typedef __attribute__((__vector_size__(3 * sizeof(unsigned)))) unsigned u32x3;
+typedef __attribute__((__vector_size__(3 * sizeof(int)))) int i32x3;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 #define LDS_AS __attribute__((address_space(3)))
 #define CONST_AS __attribute__((address_space(4)))
 
@@ -271,6 +264,13 @@ __device__ __forceinline__ void dma16(const char* gbase, unsigned voff, unsigned
                : "v"(voff), "s"(gbase), "s"(lds)
                : "memory", "m0");
 }
+// The same for 4 bytes a lane (global_load_lds_dword): they land at LDS byte lds + 4 l.
+__device__ __forceinline__ void dma4(const char* gbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
 
 // Copy j of a wave's token group: lane l's 16 bytes from gbase + voff + 128 j land at LDS byte
 // lds + 1024 j + 16 l.  The instruction offset (128 j) is added to the LDS address as well, so M0
@@ -405,117 +405,6 @@ __device__ __forceinline__ bf16x8 v_operand(unsigned tv, int db, int m) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// ---- ~6-bit cache ---------------------------------------------------------------------------------
-// Per wave and tile: rows R w .. R w + R - 1 (R = 32 / waves), copied as their contiguous codes
-// (432 bytes a row, every 16-byte piece inside one row) then their R scales; converted as units of
-// 32 codes (24 bytes) each, 18 to a row.
-template <int NW>
-struct Fp6Geom {
-  static constexpr int kRows = kTileTok / NW;
-  static constexpr int kDataBytes = kRows * kFp6RowBytes;            // 3,456 / 6,912 / 13,824
-  static constexpr int kDataCopies = (kDataBytes + 1023) / 1024;     // 4 / 7 / 14, the last partial
-  static constexpr int kCopies = kDataCopies + 1;                    // plus one for the scales
-  static constexpr int kWaveBytes = kDataBytes + kRows * 4;
-  static constexpr int kUnits = kRows * (kRow / 32);                 // 144 / 288 / 576
-  static constexpr int kRounds = (kUnits + 63) / 64;                 // 3 / 5 / 9
-  // Rounds inside the 32 steps of the output product, from step 4: loaded at 4 + kRoundStep k,
-  // converted and stored two steps later, one unit in flight at a time.
-  static constexpr int kRoundStep = 28 / kRounds > 8 ? 8 : 28 / kRounds;   // 8 / 5 / 3
-  static_assert(kRoundStep >= 3 && 4 + kRoundStep * (kRounds - 1) + 2 < 32, "rounds fit the product");
-  // Copies inside the 36 score steps: copy j at step 2 + kCopyStep j.
-  static constexpr int kCopyStep = 32 / kCopies;                                    // 6 / 4 / 2
-  static_assert(2 + kCopyStep * (kCopies - 1) < 36, "copies fit the score product");
-};
-constexpr int kFp6Stages = 3;
-
-// One 4-byte-per-lane copy HBM -> LDS: lane l's dword from gbase + voff lands at LDS byte lds + 4 l.
-__device__ __forceinline__ void dma4(const char* gbase, unsigned voff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(gbase), "s"(lds)
-               : "memory", "m0");
-}
-
-// Copy j (< kCopies) of this wave's part of one tile (tile rows start at page slot slot0, nt valid
-// rows) into its region `lds` of an fp6 stage: copies 0 .. kDataCopies - 1 move 1 KB of codes each
-// (the last one partly), the final copy the scales.  A ragged tile repeats its last valid row for
-// the missing ones, so every converted number is finite.  Some lane is active in every copy, so
-// each is one instruction for the counted waits.  j must fold to a constant.
-template <int NW>
-__device__ __forceinline__ void issue_copy6(const char* page_base, int slot0, int nt, unsigned lds, int wave, int j) {
-  using G = Fp6Geom<NW>;
-  const int ln = lane_id();
-  const int r0 = wave * G::kRows;
-  if (j < G::kDataCopies) {
-    const int o = 1024 * j + 16 * ln;
-    if (j < G::kDataCopies - 1 || o < G::kDataBytes) {
-      const int r = o / kFp6RowBytes;
-      const int rr = min(r0 + r, nt - 1);
-      dma16(page_base, (unsigned)((slot0 + rr) * kFp6RowBytes + (o - r * kFp6RowBytes)), lds + 1024 * j);
-    }
-  } else if (ln < G::kRows) {
-    dma4(page_base, (unsigned)(kPage * kFp6RowBytes + 4 * (slot0 + min(r0 + ln, nt - 1))), lds + G::kDataBytes);
-  }
-}
-
-// One conversion unit in flight: 32 codes and the row scale.
-struct Fp6Unit {
-  u32x6 codes;
-  float scale;
-};
-
-// Loads unit u of this wave's rows from its fp6 region (unit u: row u % R, codes 32 (u / R) ..,
-// R = rows per wave).  Rows vary fastest across lanes: 16 lanes then write 8 or 16 different rows,
-// which the tile swizzle spreads over the bank groups (two lanes per group with 8 rows, one with
-// 16), where 16 units of one row would land on two groups.  Units are numbered lane + 64 k for
-// round k, the lane taken from lane_id() so that the address arithmetic stays where it is used
-// instead of holding registers across the tile loop.
-template <int NW>
-__device__ __forceinline__ Fp6Unit fp6_load(unsigned region, int k) {
-  using G = Fp6Geom<NW>;
-  const int u = lane_id() + 64 * k;
-  const int r = u % G::kRows, g = u / G::kRows;
-  const LDS_AS char* src = (const LDS_AS char*)(uintptr_t)region + r * kFp6RowBytes + 24 * g;
-  const u32x2 a = *reinterpret_cast<const LDS_AS u32x2*>(src);
-  const u32x2 b = *reinterpret_cast<const LDS_AS u32x2*>(src + 8);
-  const u32x2 c = *reinterpret_cast<const LDS_AS u32x2*>(src + 16);
-  Fp6Unit x;
-  x.codes = u32x6{a[0], a[1], b[0], b[1], c[0], c[1]};
-  x.scale = *reinterpret_cast<const LDS_AS float*>((const LDS_AS char*)(uintptr_t)region + G::kDataBytes + 4 * r);
-  return x;
-}
-
-// Converts a unit (only the scale's exponent is applied, so code * 2^e exactly) and writes its 32
-// bf16 numbers, chunks 4 g .. 4 g + 3 of its row, into the swizzled bf16 tile at `stage` (1 KB
-// aligned).  Those four chunks share a block and differ only in the two low chunk bits, which the
-// swizzle XORs with a row constant: chunk 4 g + j sits at the offset of chunk 4 g XOR 16 j.  The
-// conversion is written as asm: the compiler's builtin for it returned its first element in every
-// position.
-template <int NW>
-__device__ __forceinline__ void fp6_store(const Fp6Unit& x, int k, unsigned stage, int wave) {
-  using G = Fp6Geom<NW>;
-  u32x16 v;
-  asm("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2" : "=&v"(v) : "v"(x.codes), "v"(x.scale));
-  const int u = lane_id() + 64 * k;
-  const int r = u % G::kRows, g = u / G::kRows;
-  const unsigned a0 = stage + (unsigned)tile_offset(wave * G::kRows + r, 4 * g);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    *reinterpret_cast<LDS_AS u32x4*>((LDS_AS char*)(uintptr_t)(a0 ^ (16u * j))) =
-        u32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
-}
-
-// Whole-tile conversion (prologue): every unit of this wave's rows.
-template <int NW>
-__device__ __forceinline__ void fp6_convert_all(unsigned region, unsigned stage, int wave) {
-  using G = Fp6Geom<NW>;
-  const int ln = lane_id();
-#pragma unroll
-  for (int k = 0; k < G::kRounds; ++k) {
-    if (ln + 64 * k < G::kUnits) fp6_store<NW>(fp6_load<NW>(region, k), k, stage, wave);
-  }
-}
-
 // Workgroups go to the eight XCDs round-robin (workgroup i to XCD i mod 8), each XCD with its own
 // L2.  Consecutive work units, which hold neighbouring pages and mostly the same sequence, are
 // placed on one XCD so that they share its L2 for that sequence's query and block-table lines.
@@ -524,18 +413,13 @@ __device__ __forceinline__ int xcd_unit(int id, int n) {
   return x * per + min(x, rem) + id / 8;
 }
 
-template <int NW, bool FP6, bool TOPK>
+template <int NW, bool TOPK>
 __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p) {
-  static_assert(!(FP6 && TOPK), "kept tokens are read from bf16 rows");
   constexpr int kPer = kBlocks / NW;  // copies per wave per tile
-  using G6 = Fp6Geom<NW>;
-  __shared__ __attribute__((aligned(1024))) char ring[FP6 ? 3 : kStages][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char ring[kStages][kTileBytes];
   // Target of the copies a four-wave unit issues after its last tile: they keep the count of copies
   // per tile fixed, which the counted waits rely on, and nothing reads them.
-  __shared__ __attribute__((aligned(1024))) char sink[(!FP6 && NW == 4) ? kPer * 1024 : 16];
-  // ~6-bit cache: the waves' private copy regions, three tiles' worth.
-  __shared__ __attribute__((aligned(16))) char ring6[FP6 ? kFp6Stages * NW * G6::kWaveBytes : 16];
-  auto stg = [](int t) __attribute__((always_inline)) { return FP6 ? t % 3 : stage_of(t); };
+  __shared__ __attribute__((aligned(1024))) char sink[NW == 4 ? kPer * 1024 : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -575,64 +459,23 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
 
   // Prologue: three tiles in flight.
   int issued = 0;
-  // ~6-bit cache: this wave's fp6 region for tile t, and the copies of the tile at cursor `ld`
-  const unsigned r6 = (unsigned)(uintptr_t)(LDS_AS char*)ring6 + wave * G6::kWaveBytes;
-  auto region6 = [&](int t) __attribute__((always_inline)) {
-    return r6 + (unsigned)((t % kFp6Stages) * NW * G6::kWaveBytes);
-  };
-  auto issue6 = [&](int page) __attribute__((always_inline)) {
-    const char* pb = reinterpret_cast<const char*>(p.cache) + (size_t)page * kFp6PageBytes;
-    const int slot0 = (int)((unsigned)ld.t % kPage), nt = min(kTileTok, ld.t_end - ld.t);
-    const unsigned lds = region6(issued);
 #pragma unroll
-    for (int j = 0; j < G6::kCopies; ++j) issue_copy6<NW>(pb, slot0, nt, lds, wave, j);
-    ld.advance();
-    ++issued;
-  };
-  if constexpr (FP6) {
-#pragma unroll
-    for (int s = 0; s < kFp6Stages; ++s) {
-      if (ld.valid) issue6(ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage));
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (ld.valid) {
+      issue_tile<NW, TOPK>(p, ld, (LDS_AS char*)ring[s], wave);
+      ld.advance();
+      ++issued;
     }
-    // Tiles 0 and 1 are converted here, the rest two tiles ahead inside the loop.  Once tile 0 is
-    // converted its stage takes tile 3, so the copies run four tiles ahead of the tile whose output
-    // product runs.  Loads complete in issue order, so the query has landed once tile 0 has.
-    constexpr int C = G6::kCopies;
-    if (issued >= 3) wait_vmcnt<2 * C>();
-    else if (issued == 2) wait_vmcnt<C>();
-    else wait_vmcnt<0>();
-    fp6_convert_all<NW>(region6(0), (unsigned)(uintptr_t)(LDS_AS char*)ring[0], wave);
-    if (ld.valid) issue6(ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage));
-    if (issued >= 2) {
-      if (issued >= 4) wait_vmcnt<2 * C>();
-      else if (issued == 3) wait_vmcnt<C>();
-      else wait_vmcnt<0>();
-      fp6_convert_all<NW>(region6(1), (unsigned)(uintptr_t)(LDS_AS char*)ring[1], wave);
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) {
-      if (ld.valid) {
-        issue_tile<NW, TOPK>(p, ld, (LDS_AS char*)ring[s], wave);
-        ld.advance();
-        ++issued;
-      }
-    }
-    // Loads complete in issue order: with at most the prologue's copies outstanding (capped at the
-    // counter's 63, which only waits for more), the query has landed.
-    if (issued >= 3) wait_vmcnt<(3 * kPer < 63 ? 3 * kPer : 63)>();
-    else if (issued == 2) wait_vmcnt<(2 * kPer < 63 ? 2 * kPer : 63)>();
-    else wait_vmcnt<(kPer < 63 ? kPer : 63)>();
   }
+  // Loads complete in issue order: with at most the prologue's copies outstanding (capped at the
+  // counter's 63, which only waits for more), the query has landed.
+  if (issued >= 3) wait_vmcnt<(3 * kPer < 63 ? 3 * kPer : 63)>();
+  else if (issued == 2) wait_vmcnt<(2 * kPer < 63 ? 2 * kPer : 63)>();
+  else wait_vmcnt<(kPer < 63 ? kPer : 63)>();
   // Waits until the copies of tile `t` (this wave's part) have landed, then for every wave.
   // Vector loads complete in issue order: it is enough to let the tiles issued after it stay in
   // flight.
   auto tile_ready = [&](int t) __attribute__((always_inline)) {
-    if constexpr (FP6) {  // the tile was converted by every wave: their LDS writes, then the barrier
-      wait_lgkmcnt0();
-      __builtin_amdgcn_s_barrier();
-      return;
-    }
     const int younger = issued - t - 1;
     if (younger >= 2) wait_vmcnt<(2 * kPer < 63 ? 2 * kPer : 63)>();
     else if (younger == 1) wait_vmcnt<(kPer < 63 ? kPer : 63)>();
@@ -642,7 +485,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   // Refills the stage of the tile before `t` (every wave is past it) with the next tile.
   auto refill = [&](int t) __attribute__((always_inline)) {
     if (ld.valid) {
-      issue_tile<NW, TOPK>(p, ld, (LDS_AS char*)ring[stg(t + kStages - 1)], wave);
+      issue_tile<NW, TOPK>(p, ld, (LDS_AS char*)ring[stage_of(t + kStages - 1)], wave);
       ld.advance();
       ++issued;
     }
@@ -691,7 +534,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     f32x16 s_cur;
     {
       tile_ready(it);
-      const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stg(it)] + k_off;
+      const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it)] + k_off;
       bf16x8 ka[kKAhead + 1];
 #pragma unroll
       for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tk, ks);
@@ -716,32 +559,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // repeats its last row in place of the missing ones; after the unit's last tile the copies
       // go to the sink (from the first page, which always exists).  The addresses are worked out
       // before the wait below, so that the block-table read overlaps it; the copies start after it.
-      // The ~6-bit cache copies a twelfth of the bytes per wave and issues them all at once.
       const char* sp_base = reinterpret_cast<const char*>(p.cache);
       unsigned sp_lane = 0, sp_lds = 0;
       uint64_t sp_addr = 0;  // kept tokens: this lane's full source address
       int sp_page = 0, sp_tok = 0;
       bool sp_have = false;
-      if constexpr (FP6) {
-        // The converted tile it + 1 is published by the barrier; the block-table read for the
-        // copies of tile it + 4 (into the stage of tile it + 1, converted last iteration) is issued
-        // after this wave's own LDS writes are done, so that it overlaps the barrier instead of
-        // being waited for before it.
-        wait_lgkmcnt0();
-        __builtin_amdgcn_sched_barrier(0);
-        sp_have = ld.valid;
-        if (ld.valid) {
-          sp_page = ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage);
-          sp_tok = (int)((unsigned)ld.t % kPage);
-          sp_lane = (unsigned)min(kTileTok, ld.t_end - ld.t);   // valid rows of the tile
-          sp_lds = region6(issued);
-          ld.advance();
-          ++issued;
-        }
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" : "+s"(sp_page));  // the page is first needed behind the barrier
-        if (sp_have) sp_base += (size_t)sp_page * kFp6PageBytes;
-      } else if constexpr (NW == 4) {
+      if constexpr (NW == 4) {
         const int ln = lane_id();
         const int tl = (ln >> 3) ^ (wave & 1);
         const unsigned cl16 = (unsigned)((ln & 7) ^ sigma(tl)) * 16u;
@@ -765,28 +588,20 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       }
       // The next tile must be in LDS before its scores start; the barrier also frees the stage of
       // tile it - 1.
-      if constexpr (!FP6) {
-        tile_ready(last ? it : it + 1);
-        if constexpr (NW == 4 && TOPK) {
-          ++issued;
-          asm volatile("" : "+v"(sp_addr));
-        } else if constexpr (NW == 4) {
-          ++issued;
-          asm volatile("" : "+s"(sp_page));  // the page is first needed here, behind the wait
-          if (sp_have) sp_base += ((size_t)sp_page * kPage + sp_tok) * (kRow * 2);
-        } else {
-          refill(it);
-        }
+      tile_ready(last ? it : it + 1);
+      if constexpr (NW == 4 && TOPK) {
+        ++issued;
+        asm volatile("" : "+v"(sp_addr));
+      } else if constexpr (NW == 4) {
+        ++issued;
+        asm volatile("" : "+s"(sp_page));  // the page is first needed here, behind the wait
+        if (sp_have) sp_base += ((size_t)sp_page * kPage + sp_tok) * (kRow * 2);
+      } else {
+        refill(it);
       }
       auto spread_copy = [&](int j) __attribute__((always_inline)) {
         if constexpr (NW == 4 && TOPK) dma16_addr(sp_addr, sp_lds + 1024 * j, j);
-        else if constexpr (NW == 4 && !FP6) dma16_group(sp_base, sp_lane, sp_lds, j);
-      };
-      // ~6-bit cache: copy j of tile it + 4 (spread over the score product like the bf16 copies)
-      auto copy6 = [&](int j) __attribute__((always_inline)) {
-        if constexpr (FP6) {
-          if (sp_have) issue_copy6<NW>(sp_base, sp_tok, (int)sp_lane, sp_lds, wave, j);
-        }
+        else if constexpr (NW == 4) dma16_group(sp_base, sp_lane, sp_lds, j);
       };
 
       // ---- softmax of tile it (base 2), lane = head, registers = tokens, spread over the next
@@ -830,7 +645,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       f32x16 s_nxt;
       if (!last) {
         // scores of tile it + 1 into s_nxt, one softmax step of tile it after each MFMA
-        const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stg(it + 1)] + k_off;
+        const unsigned tk = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it + 1)] + k_off;
         bf16x8 ka[kKAhead + 1];
 #pragma unroll
         for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = k_operand(tk, ks);
@@ -840,10 +655,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
           if (ks == 0) mfma_v_first_nw(s_nxt, ka[0], q[0]); else mfma_v_nw(s_nxt, ka[ks % (kKAhead + 1)], q[ks]);
           softmax_step(ks);
           if ((ks & 3) == 0) spread_copy(ks >> 2);
-          if constexpr (FP6) {
-            if (ks >= 2 && (ks - 2) % G6::kCopyStep == 0 && (ks - 2) / G6::kCopyStep < G6::kCopies)
-              copy6((ks - 2) / G6::kCopyStep);
-          }
           __builtin_amdgcn_sched_barrier(0);
         }
         mfma_v_drain(s_nxt);
@@ -852,8 +663,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
         for (int k = 0; k < 12; ++k) softmax_step(k);
 #pragma unroll
         for (int j = 0; j < kCG; ++j) spread_copy(j);
-#pragma unroll
-        for (int j = 0; j < G6::kCopies; ++j) copy6(j);
       }
 
       if (__builtin_expect(rescale, 0)) {
@@ -894,12 +703,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // then those of pb1 (the exponents of pb1 are computed during the first pass); operands
       // kVAhead MFMAs ahead.
       {
-        const unsigned tv = (unsigned)(uintptr_t)(LDS_AS char*)ring[stg(it)] + v_off;
-        // ~6-bit cache: tile it + 2 is converted here, its stage free since the barrier above
-        const bool conv = FP6 && it + 2 < issued;
-        const unsigned cv_src = FP6 ? region6(it + 2) : 0u;
-        const unsigned cv_dst = FP6 ? (unsigned)(uintptr_t)(LDS_AS char*)ring[stg(it + 2)] : 0u;
-        Fp6Unit cbuf;
+        const unsigned tv = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it)] + v_off;
         bf16x8 va[kVAhead + 1];
 #pragma unroll
         for (int i = 0; i < kVAhead; ++i) va[i] = v_operand(tv, i & 15, i >> 4);
@@ -913,22 +717,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
           else mfma_a_nw(o[i & 15], va[i % (kVAhead + 1)], pb1);
           if (i < 8) softmax_exp(8 + i);
           if (i == 8) l_sum += ls0 + ls1;
-          if constexpr (FP6) {
-            if (conv) {
-              if (i == 4) {  // this wave's copies of tile it + 2 have landed (those of it + 3, it + 4 may not)
-                if (it + 4 < issued) wait_vmcnt<2 * G6::kCopies>();
-                else if (it + 3 < issued) wait_vmcnt<G6::kCopies>();
-                else wait_vmcnt<0>();
-              }
-#pragma unroll
-              for (int k = 0; k < G6::kRounds; ++k) {
-                const int at = 4 + k * G6::kRoundStep;
-                const bool mine = lane + 64 * k < G6::kUnits;
-                if (i == at && mine) cbuf = fp6_load<NW>(cv_src, k);
-                if (i == at + 2 && mine) fp6_store<NW>(cbuf, k, cv_dst, wave);
-              }
-            }
-          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -960,7 +748,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // against bank conflicts, and passes its rows through a quarter at a time.
       constexpr int kPad = 256 + 16;
       __builtin_amdgcn_s_barrier();
-      LDS_AS char* region = (LDS_AS char*)ring[stg(it - 1)] + wave * 32 * kPad;
+      LDS_AS char* region = (LDS_AS char*)ring[stage_of(it - 1)] + wave * 32 * kPad;
       const int hw = ln & 31, hl = ln >> 5;
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
@@ -985,6 +773,415 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   wait_vmcnt<0>();
 }
 
+// ---- ~6-bit cache, read from its codes -----------------------------------------------------------
+// A tile of 32 rows lands in LDS as 40 sixteen-byte slots per row (row stride 640 bytes): slot p of
+// row t holds code chunk c (codes 16 c .. 16 c + 15, 12 bytes, copied as 16 bytes from the packed
+// row, so that every chunk starts on a 16-byte boundary), c = (p & ~7) | ((p & 7) ^ f6swz(t)); slots
+// whose c is 36 or more are padding.  The rows' fp32 scales follow at byte 20,480.
+//   scores: lane (token t, half h) converts codes 64 j + 32 h .. + 31 of its token (chunks 4 j + 2 h
+//     and + 1, two 12-byte reads) with v_cvt_scalef32_pk32_bf16_fp6 and the row's scale (exact:
+//     code x 2^e), giving its A operands of k-steps 4 j .. 4 j + 3; the query is loaded in the same
+//     k order (dims 64 j + 32 h + 8 i of k-step 4 j + i).
+//   output: ds_read_b96_tr_b6 gives each lane of a 16-lane group one code column (one latent dim)
+//     of the 16 rows whose addresses the group's lanes supply: lanes of half h supply tokens
+//     4 h + 8 (e / 4) + e % 4, e = 0 .. 15, the order of the probabilities the lane holds, and two
+//     d-blocks' reads convert at scale 1 into the A operands of both output MFMAs of both blocks.
+//     The rows' scales 2^e_t move onto the probabilities instead (exact in bf16 but for values
+//     below 2^-125, which add nothing).
+// The swizzle f6swz spreads the 32 rows of a score read over 8 slots per 8 rows and the 16 rows of
+// one transposing read over pairs of slots.
+constexpr int kF6Slots = 40;                        // 16-byte slots per row in LDS
+constexpr int kF6RowStride = kF6Slots * 16;         // 640
+constexpr int kF6ScaleOff = kTileTok * kF6RowStride;  // 20,480: the rows' fp32 scales
+constexpr int kF6DataCopies = kTileTok * kF6Slots / 64;  // 20 copies of 64 slots per tile
+
+__device__ __forceinline__ int f6swz(int t) { return (t & 3) | ((((t >> 2) ^ (t >> 3)) & 1) << 2); }
+
+// Byte offset, inside a packed ~6-bit page row block, of the source of LDS slot g (0 .. 1,279) of a
+// tile: row min(g / 40, nt - 1), chunk c (chunk 0 for padding slots).
+__device__ __forceinline__ unsigned f6_src_off(int g, int nt) {
+  const int t = g / kF6Slots, slot = g % kF6Slots;
+  int c = (slot & ~7) | ((slot & 7) ^ f6swz(t));
+  if (c >= kRow / 16) c = 0;
+  return (unsigned)(min(t, nt - 1) * kFp6RowBytes + 12 * c);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void decode_fp6_kernel(DecodeParams p) {
+  constexpr int kDataPer = kF6DataCopies / NW;      // 5 (four waves) or 10 (two waves)
+  constexpr int kPer = kDataPer + 1;                // plus this wave's rows' scales
+  constexpr int kScaleRows = kTileTok / NW;         // scales this wave copies
+  static_assert(kF6DataCopies % NW == 0, "whole copies per wave");
+  __shared__ __attribute__((aligned(1024))) char ring[kStages][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sink[1024];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int w = uni(xcd_unit(blockIdx.x, gridDim.x));
+
+  TileCursor ld, cp;
+  ld.init(p, w);
+  cp = ld;
+  if (!cp.valid) return;
+
+  // Score operand: row l32, chunk pair 4 j + 2 half: two lane offsets (j even / odd); the second
+  // chunk of a pair is the slot XOR 1 (byte XOR 16), and j / 2 adds 128 bytes.
+  unsigned ko[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) ko[par] = (unsigned)(l32 * kF6RowStride + 16 * ((4 * par + 2 * half) ^ f6swz(l32)));
+  // Output operand: this lane supplies the row of token 4 (lane / 32) + 8 (e / 4) + e % 4, e = lane
+  // % 16, for chunk 2 db + (lane / 16) % 2; four lane offsets (db % 4), db / 4 adds 128 bytes.
+  unsigned vo[4];
+  {
+    const int e = lane & 15, g = lane >> 4;
+    const int tv = 4 * (g >> 1) + 8 * (e >> 2) + (e & 3);
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4) vo[d4] = (unsigned)(tv * kF6RowStride + 16 * ((2 * d4 + (g & 1)) ^ f6swz(tv)));
+  }
+  // Source offsets of this wave's data copies for a full tile (row 0 = the tile's first row).
+  unsigned so[kDataPer];
+#pragma unroll
+  for (int j = 0; j < kDataPer; ++j) so[j] = f6_src_off(64 * (wave * kDataPer + j) + lane, kTileTok);
+
+  const uint16_t* qa = static_cast<const uint16_t*>(p.q_abs);
+  bf16x8 q[36];
+  auto load_q = [&](int b) __attribute__((always_inline)) {
+    const int ln = lane_id();
+    const uint16_t* qrow = qa + ((size_t)b * p.heads + wave * 32 + (ln & 31)) * kRow + 32 * (ln >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 64 * (ks >> 2) + 8 * (ks & 3));
+  };
+  load_q(cp.b);
+
+  // Copies of the tile at cursor c into LDS stage `lds` (sink when !have): data copy j of this wave,
+  // then (j == kDataPer) its rows' scales.  j must fold to a constant.
+  auto copy = [&](bool have, const char* pb, int slot0, int nt, unsigned lds, int j) __attribute__((always_inline)) {
+    const char* rows = pb + (size_t)slot0 * kFp6RowBytes;
+    if (j < kDataPer) {
+      const unsigned off = (have && nt < kTileTok) ? f6_src_off(64 * (wave * kDataPer + j) + lane_id(), nt) : so[j];
+      dma16(rows, off, have ? lds + 1024 * (wave * kDataPer + j) : (unsigned)(uintptr_t)(LDS_AS char*)sink);
+    } else {
+      const int ln = lane_id();
+      if (ln < kScaleRows) {
+        const int r = wave * kScaleRows + ln;
+        dma4(pb + kPage * kFp6RowBytes, (unsigned)(4 * (slot0 + min(r, nt - 1))),
+             have ? lds + kF6ScaleOff + 4 * wave * kScaleRows : (unsigned)(uintptr_t)(LDS_AS char*)sink);
+      }
+    }
+  };
+  auto page_of_ld = [&]() __attribute__((always_inline)) {
+    return reinterpret_cast<const char*>(p.cache) +
+           (size_t)ld_const(p.block_table, (size_t)ld.b * p.max_blocks + (unsigned)ld.t / kPage) * kFp6PageBytes;
+  };
+
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (ld.valid) {
+      const char* pb = page_of_ld();
+      const int slot0 = (int)((unsigned)ld.t % kPage), nt = min(kTileTok, ld.t_end - ld.t);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) copy(true, pb, slot0, nt, (unsigned)(uintptr_t)(LDS_AS char*)ring[s], j);
+      ld.advance();
+      ++issued;
+    }
+  }
+  if (issued >= 3) wait_vmcnt<3 * kPer>();
+  else if (issued == 2) wait_vmcnt<2 * kPer>();
+  else wait_vmcnt<kPer>();
+  auto tile_ready = [&](int t) __attribute__((always_inline)) {
+    const int younger = issued - t - 1;
+    if (younger >= 2) wait_vmcnt<2 * kPer>();
+    else if (younger == 1) wait_vmcnt<kPer>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+  auto tail_masked = [&](const f32x16& s, int n) __attribute__((always_inline)) {
+    f32x16 r;
+    const int hf = lane_id() >> 5;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = ((j >> 2) * 8 + hf * 4 + (j & 3) >= n) ? -INFINITY : s[j];
+    return r;
+  };
+  // Score operands of k-steps 4 j .. 4 j + 3 from stage st: two 12-byte reads and a conversion.
+  auto k_conv_read = [&](unsigned st, int j, u32x6& codes) __attribute__((always_inline)) {
+    const LDS_AS char* a = (const LDS_AS char*)(uintptr_t)(st + ko[j & 1] + 128 * (j >> 1));
+    const u32x3 c0 = *reinterpret_cast<const LDS_AS u32x3*>(a);
+    const u32x3 c1 = *reinterpret_cast<const LDS_AS u32x3*>((const LDS_AS char*)(uintptr_t)((st + ko[j & 1] + 128 * (j >> 1)) ^ 16u));
+    codes = u32x6{c0[0], c0[1], c0[2], c1[0], c1[1], c1[2]};
+  };
+  auto cvt32 = [&](const u32x6& codes, float sc) __attribute__((always_inline)) {
+    u32x16 v;
+    asm volatile("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2" : "=&v"(v) : "v"(codes), "v"(sc));
+    return v;
+  };
+  // The same with wait states after it, for a result that an MFMA reads next.
+  auto cvt32_w = [&](const u32x6& codes, float sc) __attribute__((always_inline)) {
+    u32x16 v;
+    asm volatile("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2\n\ts_nop 4" : "=&v"(v) : "v"(codes), "v"(sc));
+    return v;
+  };
+  auto op4 = [](const u32x16& v, int i) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, u32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]});
+  };
+  // Score product of the tile in stage st into s (36 MFMAs, conversions one group ahead); `step(ks)`
+  // runs after each MFMA.
+  auto scores = [&](unsigned st, f32x16& sacc, auto&& step) __attribute__((always_inline)) {
+    const float sc = *reinterpret_cast<const LDS_AS float*>((const LDS_AS char*)(uintptr_t)(st + kF6ScaleOff + 4 * l32));
+    u32x6 cd;
+    k_conv_read(st, 0, cd);
+    u32x16 cur = cvt32_w(cd, sc);
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      u32x16 nxt;
+      if (j + 1 < 9) k_conv_read(st, j + 1, cd);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ks = 4 * j + i;
+        if (ks == 0) mfma_v_first(sacc, op4(cur, 0), q[0]);
+        else mfma_v(sacc, op4(cur, i), q[ks]);
+        step(ks);
+        if (i == 1 && j + 1 < 9) nxt = cvt32(cd, sc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j + 1 < 9) cur = nxt;
+    }
+    mfma_v_drain(sacc);
+  };
+  auto no_step = [](int) __attribute__((always_inline)) {};
+
+  const float scale = p.scale_log2;
+  int it = 0;
+  bool first_segment = true;
+  while (cp.valid) {
+    const int b = cp.b;
+    if (threadIdx.x == 0) {
+      if (cp.t == 0) {
+        p.seq_units[4 * b] = w;
+        p.seq_units[4 * b + 2] = cp.all_live ? 1 : 0;
+      }
+      if (cp.t_end == cp.len) p.seq_units[4 * b + 1] = w;
+    }
+    if (!first_segment) {
+      load_q(b);
+      wait_vmcnt<0>();
+    }
+    first_segment = false;
+    f32x16 o[16];
+    {
+      const bf16x8 zero = {};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mfma_a_zero(o[i], zero);
+    }
+    float m_ref = -INFINITY;
+    float l_sum = 0.f;
+    bool fresh = true;
+
+    f32x16 s_cur;
+    {
+      tile_ready(it);
+      scores((unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it)], s_cur, no_step);
+      const int n0 = min(kTileTok, cp.t_end - cp.t);
+      if (n0 < kTileTok) s_cur = tail_masked(s_cur, n0);
+    }
+
+    bool last;
+    do {
+      last = cp.last();
+      cp.advance();
+      // copies of tile it + 3 into the stage of tile it - 1 (the sink after the unit's last tile),
+      // spread over the score MFMAs below
+      const bool sp_have = ld.valid;
+      const char* sp_pb = reinterpret_cast<const char*>(p.cache);
+      int sp_slot0 = 0, sp_nt = kTileTok;
+      if (sp_have) {
+        sp_pb = page_of_ld();
+        sp_slot0 = (int)((unsigned)ld.t % kPage);
+        sp_nt = min(kTileTok, ld.t_end - ld.t);
+        ld.advance();
+      }
+      const unsigned sp_lds = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it + kStages - 1)];
+      tile_ready(last ? it : it + 1);
+      ++issued;
+      asm volatile("" : "+s"(sp_pb));
+      auto spread_copy = [&](int ks) __attribute__((always_inline)) {
+        constexpr int kEvery = 32 / kPer;   // six copies: every 5 k-steps; eleven: every 2
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if (ks == kEvery * j) copy(sp_have, sp_pb, sp_slot0, sp_nt, sp_lds, j);
+      };
+
+      // probabilities of tile it carry the tokens' scales 2^e_t: this lane's 16 tokens are
+      // 4 half + 8 k + 0 .. 3, k = 0 .. 3, four consecutive scales read together one group ahead
+      const unsigned sb = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it)] + kF6ScaleOff + 16 * half;
+      auto tsc_read = [&](int k) __attribute__((always_inline)) {
+        return *reinterpret_cast<const LDS_AS f32x4*>((const LDS_AS char*)(uintptr_t)(sb + 32 * k));
+      };
+      f32x4 tsc_cur = tsc_read(0), tsc_nxt = tsc_read(1);
+      float mt, ls0 = 0.f, ls1 = 0.f, alpha = 1.f;
+      bool rescale = false;
+      bf16x8 pb0, pb1;
+      auto softmax_exp = [&](int j) __attribute__((always_inline)) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s_cur[j], scale, -m_ref));
+        if (j & 1) ls1 += e; else ls0 += e;
+        const float pe = e * tsc_cur[j & 3];
+        if (j < 8) pb0[j] = (__bf16)pe; else pb1[j - 8] = (__bf16)pe;
+        if ((j & 3) == 3 && j < 15) {
+          tsc_cur = tsc_nxt;
+          if (j + 5 < 16) tsc_nxt = tsc_read((j + 5) >> 2);
+        }
+      };
+      auto softmax_step = [&](int k) __attribute__((always_inline)) {
+        if (k == 0) {
+          mt = max3(max3(s_cur[0], s_cur[1], s_cur[2]), max3(s_cur[3], s_cur[4], s_cur[5]),
+                    max2(s_cur[6], s_cur[7]));
+        } else if (k == 1) {
+          mt = max3(max3(mt, s_cur[8], s_cur[9]), max3(s_cur[10], s_cur[11], s_cur[12]),
+                    max3(s_cur[13], s_cur[14], s_cur[15]));
+        } else if (k == 2) {
+          mt = max_halves(mt) * scale;
+        } else if (k == 3) {
+          if (fresh) {
+            m_ref = mt;
+            fresh = false;
+          } else if (__ballot(mt > m_ref + kRescaleThreshold)) {
+            const float m_new = fmaxf(m_ref, mt);
+            alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            l_sum *= alpha;
+            rescale = true;
+          }
+        } else if (k >= 4 && k < 4 + 16) {  // all 16 probabilities before the output product
+          softmax_exp(k - 4);
+        } else if (k == 4 + 16) {
+          l_sum += ls0 + ls1;
+        }
+      };
+
+      f32x16 s_nxt;
+      if (!last) {
+        scores((unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it + 1)], s_nxt, [&](int ks) __attribute__((always_inline)) {
+          softmax_step(ks);
+          spread_copy(ks);
+        });
+      } else {
+#pragma unroll
+        for (int k = 0; k < 21; ++k) softmax_step(k);
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) spread_copy(ks);
+      }
+
+      if (__builtin_expect(rescale, 0)) {
+        mfma_a_drain(o);
+        const int ln = lane_id();
+        float* slot = p.ws_o + (((size_t)w + b) * p.heads + wave * 32 + (ln & 31)) * kDc + 4 * (ln >> 5);
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(slot + 32 * db + 8 * g) =
+                make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+          f32x16 t;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 v = *reinterpret_cast<const float4*>(slot + 32 * db + 8 * g);
+            t[4 * g] = v.x * alpha;
+            t[4 * g + 1] = v.y * alpha;
+            t[4 * g + 2] = v.z * alpha;
+            t[4 * g + 3] = v.w * alpha;
+          }
+          o[db] = t;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        load_q(b);
+        wait_vmcnt<0>();
+      }
+
+      // output of tile it: per pair of d-blocks, two transposing reads and one conversion at scale
+      // 1 give the A operands of four MFMAs; the next pair is read two pairs ahead and converted
+      // while the current pair's MFMAs run, so no MFMA reads a register the conversion just wrote
+      {
+        const unsigned tv = (unsigned)(uintptr_t)(LDS_AS char*)ring[stage_of(it)];
+        auto vread = [&](int db) __attribute__((always_inline)) {
+          return __builtin_amdgcn_ds_read_tr6_b96_v3i32(
+              (LDS_AS i32x3*)((LDS_AS char*)(uintptr_t)(tv + vo[db & 3] + 128 * (db >> 2))));
+        };
+        auto pair_codes = [](const i32x3& a, const i32x3& c) __attribute__((always_inline)) {
+          return u32x6{(unsigned)a[0], (unsigned)a[1], (unsigned)a[2], (unsigned)c[0], (unsigned)c[1], (unsigned)c[2]};
+        };
+        i32x3 r0 = vread(0), r1 = vread(1);
+        u32x16 vcur = cvt32_w(pair_codes(r0, r1), 1.0f);
+        r0 = vread(2);
+        r1 = vread(3);
+#pragma unroll
+        for (int pr = 0; pr < 8; ++pr) {
+          const int d0 = 2 * pr, d1 = 2 * pr + 1;
+          u32x16 vnxt;
+          mfma_a(o[d0], op4(vcur, 0), pb0);
+          mfma_a_nw(o[d1], op4(vcur, 2), pb0);
+          if (pr + 1 < 8) {
+            vnxt = cvt32(pair_codes(r0, r1), 1.0f);
+            if (pr + 2 < 8) {
+              r0 = vread(2 * pr + 4);
+              r1 = vread(2 * pr + 5);
+            }
+          }
+          mfma_a_nw(o[d0], op4(vcur, 1), pb1);
+          mfma_a_nw(o[d1], op4(vcur, 3), pb1);
+          if (pr + 1 < 8) vcur = vnxt;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (!last) {
+        const int nn = min(kTileTok, cp.t_end - cp.t);
+        s_cur = nn < kTileTok ? tail_masked(s_nxt, nn) : s_nxt;
+      }
+      ++it;
+    } while (!last);
+
+    const float l_tot = sum_halves(l_sum);
+    const float inv = 1.f / l_tot;
+    mfma_a_drain(o);
+    const int ln = lane_id();
+    const size_t part = ((size_t)w + b) * p.heads + wave * 32 + (ln & 31);
+    auto packed_out = [&](int db, int g) __attribute__((always_inline)) {
+      const bf16x4 v = {(__bf16)(o[db][4 * g] * inv), (__bf16)(o[db][4 * g + 1] * inv),
+                        (__bf16)(o[db][4 * g + 2] * inv), (__bf16)(o[db][4 * g + 3] * inv)};
+      return __builtin_bit_cast(u32x2, v);
+    };
+    {
+      constexpr int kPad = 256 + 16;
+      __builtin_amdgcn_s_barrier();
+      LDS_AS char* region = (LDS_AS char*)ring[stage_of(it - 1)] + wave * 32 * kPad;
+      const int hw = ln & 31, hl = ln >> 5;
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<LDS_AS u32x2*>(region + hw * kPad + (32 * d + 8 * g + 4 * hl) * 2) = packed_out(4 * qt + d, g);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int h = 4 * k + (ln >> 4);
+          const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(region + h * kPad + (ln & 15) * 16);
+          const size_t ph = ((size_t)w + b) * p.heads + wave * 32 + h;
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.ws_o + ph * kDc) + 128 * qt + 8 * (ln & 15)) = v;
+        }
+      }
+    }
+    if (ln < 32) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_ref, l_tot);
+  }
+  wait_vmcnt<0>();
+}
+
 }  // namespace
 
 bool mfma_supported(const DecodeParams& p) {
@@ -994,30 +1191,28 @@ bool mfma_supported(const DecodeParams& p) {
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
   if (p.fp6) {
     if (p.positions) return hipErrorNotSupported;
-    // No one-wave variant: with its conversion the compiler keeps that kernel's output accumulators
-    // in memory across the tile loop, which the unpadded MFMA wrappers above do not allow.
     switch (p.heads) {
-      case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, true, false>), dim3(p.num_units), dim3(256), 0, s, p); break;
-      case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, true, false>), dim3(p.num_units), dim3(128), 0, s, p); break;
+      case 128: hipLaunchKernelGGL((decode_fp6_kernel<4>), dim3(p.num_units), dim3(256), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((decode_fp6_kernel<2>), dim3(p.num_units), dim3(128), 0, s, p); break;
       default: return hipErrorNotSupported;
     }
     return hipGetLastError();
   }
   if (p.positions) {
     switch (p.heads) {
-      case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false, true>), dim3(p.num_units), dim3(256), 0, s, p); break;
-      case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false, true>), dim3(p.num_units), dim3(128), 0, s, p); break;
+      case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, true>), dim3(p.num_units), dim3(256), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, true>), dim3(p.num_units), dim3(128), 0, s, p); break;
       case 32:
-      case 16: hipLaunchKernelGGL((decode_mfma_kernel<1, false, true>), dim3(p.num_units), dim3(64), 0, s, p); break;
+      case 16: hipLaunchKernelGGL((decode_mfma_kernel<1, true>), dim3(p.num_units), dim3(64), 0, s, p); break;
       default: return hipErrorNotSupported;
     }
     return hipGetLastError();
   }
   switch (p.heads) {
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false, false>), dim3(p.num_units), dim3(256), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false, false>), dim3(p.num_units), dim3(128), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false>), dim3(p.num_units), dim3(256), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false>), dim3(p.num_units), dim3(128), 0, s, p); break;
     case 32:
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<1, false, false>), dim3(p.num_units), dim3(64), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<1, false>), dim3(p.num_units), dim3(64), 0, s, p); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
