@@ -309,11 +309,13 @@ def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_
                             "speedup_vs_dense": round(dense_ms / ms_gather_path, 3)}}
 
 
-def measured_peaks(dev):
-    """What this GPU reaches on plain library work, as the second reference the roofline fractions are
-    quoted against: a 2 GiB device copy (bytes read + written; torch's float32 sum over the same
-    array reads at only about 4 TB/s, so it is no measure of the peak) and an 8,192-cube bf16 matrix
-    product (torch / hipBLASLt).  Each timed with HIP events, best of five after two untimed runs."""
+def measured_peaks(dev, lib=None):
+    """What this GPU reaches on plain work, as the second reference the roofline fractions are quoted
+    against: a 2 GiB device copy (bytes read + written; torch's float32 sum over the same array reads
+    at only about 4 TB/s, so it is no measure of the peak), an 8,192-cube bf16 matrix product (torch /
+    hipBLASLt), and the matrix-core rate itself (mla_calibrate_mfma: every SIMD issuing independent
+    v_mfma_f32_32x32x16_bf16 back to back, the decode's instruction).  Each timed with HIP events,
+    best of five after two untimed runs."""
     import torch
 
     def best(fn, reps=5):
@@ -341,8 +343,16 @@ def measured_peaks(dev):
     tf = 2 * m ** 3 / best(lambda: torch.matmul(a, b)) / 1e12
     del a, b
     torch.cuda.empty_cache()
-    return {"hbm_copy_gbs": round(copy_gbs, 1), "mfma_bf16_tflops": round(tf, 1),
-            "how": "2 GiB device copy (read + write bytes); 8192^3 bf16 matmul; best of 5"}
+    out = {"hbm_copy_gbs": round(copy_gbs, 1), "mfma_bf16_tflops": round(tf, 1),
+           "how": "2 GiB device copy (read + write bytes); 8192^3 bf16 matmul; best of 5"}
+    if lib is not None:
+        blocks, iters = 1024, 4096
+        buf = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+        t = best(lambda: lib.mla_calibrate_mfma(buf, blocks, iters))
+        out["mfma_issue_bf16_tflops"] = round(blocks * 4 * iters * 4 * 32 * 32 * 16 * 2 / t / 1e12, 1)
+        out["how"] += ("; mla_calibrate_mfma: 1,024 workgroups x 4 waves x 16,384 independent "
+                       "v_mfma_f32_32x32x16_bf16 each")
+    return out
 
 
 def cpu_baseline(wl, seconds: float):
@@ -514,6 +524,56 @@ class Resident:
             self.layer(lib, d, marks, separate)
 
 
+def graph_timing(lib, res: Resident, steps: int) -> dict:
+    """The step, and mla_decode alone, captured in HIP graphs and replayed: the kernels run back to
+    back, without the host's per-call work (argument checks, marshalling, launches) between them,
+    which is what a serving loop that replays a captured decode step sees.  One capture covers one
+    step per input set (all layers of a multi-layer step); the replays are timed between two
+    synchronisations.  Each graph's first replay is checked against the eager calls' outputs."""
+    import torch
+    wl = res.wl
+    n_cap = 1 if res.layers > 1 else res.sets
+    reps = max(2, steps // n_cap)
+    out = {"how": "torch.cuda.CUDAGraph capture of the library calls, replays between synchronisations"}
+
+    def timed(g, per):
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / (reps * per)
+
+    # eager reference of the last captured step's output, then the captured form
+    for i in range(n_cap):
+        res.step(lib, i)
+    torch.cuda.synchronize()
+    ref = res.out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_cap):
+            res.step(lib, i)
+    res.out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(ref.view(torch.int16), res.out.view(torch.int16)):
+        raise RuntimeError("graph replay of the step differs from the eager step")
+    out["ms_per_step"] = round(timed(g, n_cap), 5)
+    del g
+    ds = res.inst[:res.layers] if res.layers > 1 else res.inst[:res.sets]
+    gd = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gd):
+        for d in ds:
+            res.decode(lib, d)
+    ms = timed(gd, len(ds))
+    del gd
+    gbs = res.cache_bytes / (ms * 1e-3) / 1e9
+    out["decode_call"] = {"ms_per_launch": round(ms, 5), "achieved": round(gbs, 2), "unit": "GB/s",
+                          "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def time_workload(lib, res: Resident, steps: int, warmup: int) -> dict:
     """Whole steps between two synchronisations (nothing but the path's kernels on the stream); a
     second pass of the same steps with HIP events around every call of every layer, on the stream
@@ -566,6 +626,7 @@ def time_workload(lib, res: Resident, steps: int, warmup: int) -> dict:
             blocks[sep].append((time.perf_counter() - t0) * 1e3 / steps)
     ms_sep = sorted(blocks[True])[1]
     ms_one = sorted(blocks[False])[1]
+    graph = graph_timing(lib, res, steps)
 
     N = wl.tokens
     decode_flops = N * 2 * wl.heads * (D_C + D_R + D_C)
@@ -601,6 +662,7 @@ def time_workload(lib, res: Resident, steps: int, warmup: int) -> dict:
                         "ms_per_launch": round(dec_ms, 5), "ms_per_launch_median": round(dec_med, 5),
                         "mfma_tflops": round(dec_tf, 2), "mfma_frac": round(dec_tf / MFMA_BF16_PEAK_TF, 4)},
         "calls_per_layer": calls,
+        "graph": graph,
     }
     # Warm numbers, labelled: when the cache fits in the 256 MB Infinity Cache, the same input set
     # every call (the steps above rotate sets so that each call reads HBM).
@@ -724,7 +786,7 @@ def main():
                             ("sparse_topk", "fp6", "out_proj_hidden", "producer"))
     del res
     torch.cuda.empty_cache()
-    peaks = measured_peaks(dev)
+    peaks = measured_peaks(dev, lib)
     dc = main_rec["decode_call"]
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -740,10 +802,12 @@ def main():
         "roofline": dict(dc, kernel="mla_decode (decode + merge kernels, one call per layer)",
                          measured_peaks=peaks,
                          frac_of_measured_copy=round(dc["achieved"] / peaks["hbm_copy_gbs"], 4),
-                         mfma_frac_of_measured=round(dc["mfma_tflops"] / peaks["mfma_bf16_tflops"], 4)),
+                         mfma_frac_of_measured=round(dc["mfma_tflops"] / peaks["mfma_bf16_tflops"], 4),
+                         mfma_frac_of_issue_rate=round(dc["mfma_tflops"] / peaks["mfma_issue_bf16_tflops"], 4)),
         "calls_per_layer": main_rec["calls_per_layer"],
         "ms_per_step_separate_calls": main_rec["ms_per_step_separate_calls"],
         "ms_per_step_one_call_alternating": main_rec["ms_per_step_one_call_alternating"],
+        "graph": main_rec["graph"],
     }
     line["roofline"].pop("kernels", None)
     line.update(side)

@@ -22,7 +22,7 @@ EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", 
            "mla_absorb_q", "mla_decode", "mla_out_proj", "mla_cache_append_hidden_workspace_size",
            "mla_cache_append_hidden", "mla_cache_append_fp6", "mla_cache_quantize_fp6", "mla_decode_fp6",
            "mla_out_proj_hidden_workspace_size", "mla_out_proj_hidden", "mla_index_topk_workspace_size",
-           "mla_index_topk", "mla_gather_rows", "mla_decode_topk_workspace_size", "mla_decode_topk", "mla_decode_noalloc_max_bytes",
+           "mla_index_topk", "mla_gather_rows", "mla_decode_topk_workspace_size", "mla_decode_topk", "mla_decode_noalloc_max_bytes", "mla_calibrate_mfma",
            "mla_decode_noalloc", "mla_decode_out_proj_workspace_size", "mla_decode_out_proj")
 INDEX_DIM = 128          # MLA_INDEX_DIM: int8 numbers in a token's index vector
 FP6_PAGE_BYTES = 27904   # MLA_FP6_PAGE_BYTES: 64 rows of 432 code bytes, then 64 float32 scales
@@ -45,6 +45,8 @@ lib.mla_absorb_q.restype = _i
 lib.mla_absorb_q.argtypes = [_p, _p, _p, _i, _i, _i, _p]
 lib.mla_decode.restype = _i
 lib.mla_decode.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _p, _sz, _i, _i, _p]
+lib.mla_calibrate_mfma.restype = _i
+lib.mla_calibrate_mfma.argtypes = [_p, _i, _i, _p]
 lib.mla_decode_noalloc_max_bytes.restype = _sz
 lib.mla_decode_noalloc_max_bytes.argtypes = []
 lib.mla_decode_noalloc.restype = _i
@@ -212,6 +214,14 @@ def mla_decode(q_abs, kv_cache, block_table, seq_lens, softmax_scale, o_lat, lse
                           _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, H,
                           float(softmax_scale), _ptr(o_lat), _ptr(lse), _ptr(workspace), ws_bytes,
                           int(num_splits), _dtype_of(q_abs), _stream(stream)), "mla_decode")
+
+
+def mla_calibrate_mfma(out, blocks: int, iters: int, stream=None):
+    """out: float32 device tensor of at least blocks * 4 elements; see the header for the rate."""
+    _dev(out)
+    if out.dtype != torch.float32 or out.numel() < 4 * blocks:
+        raise ValueError("out must be a float32 tensor of at least blocks * 4 elements")
+    _check(lib.mla_calibrate_mfma(_ptr(out), int(blocks), int(iters), _stream(stream)), "mla_calibrate_mfma")
 
 
 def mla_decode_noalloc_max_bytes() -> int:

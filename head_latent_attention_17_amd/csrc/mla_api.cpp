@@ -61,7 +61,7 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_abi_version(void) { return 106; }
+int mla_abi_version(void) { return 107; }
 
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype) {
@@ -276,6 +276,12 @@ mla_status mla_decode_out_proj(const void* q_abs, const void* kv_cache, int num_
 }
 
 size_t mla_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+mla_status mla_calibrate_mfma(float* out, int blocks, int iters, hipStream_t stream) {
+  if (!out) return MLA_ERR_NULL;
+  if (blocks < 1 || iters < 1) return MLA_ERR_SHAPE;
+  return launch_mfma_rate(out, blocks, iters, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
 
 mla_status mla_decode_noalloc(const void* q_abs, const void* kv_cache, int num_pages, int page_size,
                               const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,

@@ -104,6 +104,9 @@ hipError_t check_positions(const int32_t* block_table, int max_blocks, const int
 // (append = true); synchronises s.  *bad is set when an entry is out of range.
 hipError_t check_tables(const int32_t* block_table, int max_blocks, const int32_t* lens, int batch,
                         int num_pages, bool append, hipStream_t s, bool* bad);
+// Matrix-core rate kernel: `blocks` workgroups of four waves, each wave `iters` x 4 independent
+// v_mfma_f32_32x32x16_bf16; out holds one float per wave (blocks * 4).
+hipError_t launch_mfma_rate(float* out, int blocks, int iters, hipStream_t s);
 // Device address of this device's fixed scratch array (kNoAllocScratchBytes), looked up on the first
 // call on each device; allocates nothing.
 hipError_t noalloc_scratch(void** out);

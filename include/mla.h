@@ -313,6 +313,18 @@ mla_status mla_decode_topk(const void* q_abs, const void* kv_cache, int num_page
                            const int32_t* counts, int batch, int k, int num_heads, float softmax_scale,
                            void* o_lat, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Matrix-core rate calibration (for reading the decode's roofline; not part of the decode path).
+ * Launches `blocks` workgroups of four waves on `stream`; every wave issues iters x 4 independent
+ * v_mfma_f32_32x32x16_bf16 products (32 x 32 x 16 multiply-adds each) back to back, touching no
+ * memory but its one result: out[w] (float, device, blocks * 4 of them, written) for wave w.  The
+ * caller times the launch (for example with events on the stream):
+ * rate = blocks * 4 * iters * 4 * 32,768 flops / duration.  With blocks a multiple of the compute
+ * units every SIMD runs one such wave.  Errors: MLA_ERR_NULL (out), MLA_ERR_SHAPE (blocks < 1 or
+ * iters < 1), MLA_ERR_HIP.
+ */
+mla_status mla_calibrate_mfma(float* out, int blocks, int iters, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.mla_abi_version() == 106
+    assert L.mla_abi_version() == 107
     for code, name in L.STATUS.items():
         assert L.mla_status_string(code).startswith(name)
     assert "unknown" in L.mla_status_string(12345)
