@@ -70,6 +70,10 @@ def parse():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-side-records", action="store_true",
+                    help="skip the further calls on the main workload (top-k, ~6-bit, hidden-width "
+                         "projection, producer): for kernel traces whose per-kernel averages must "
+                         "hold only the step's own dispatches")
     ap.add_argument("--profile-run", action="store_true",
                     help="for counter runs: a few untimed steps, then mla_decode alone, then "
                          "mla_decode_out_proj, then mla_decode_fp6 over the cache's ~6-bit form, "
@@ -781,7 +785,7 @@ def main():
     step_flops = layers * (decode_flops + proj_flops)
     value = layers * res.cache_bytes / (ms_step * 1e-3) / 1e9
     side = {}
-    if layers == 1:
+    if layers == 1 and not args.no_side_records:
         side = side_records(lib, synth, res, dev, args.steps,
                             ("sparse_topk", "fp6", "out_proj_hidden", "producer"))
     del res
