@@ -9,6 +9,9 @@
 // slab ahead into registers; the two K halves of its four waves are summed through LDS into an
 // fp32 partial tile.  A second kernel sums the partials in chunk order and rounds to bf16.  Batches
 // above 64 rows go through in groups of 64 (each group streams the weights again).
+// Batches up to 32 take a wide form instead (dense_proj4_kernel): 128-column blocks whose copies
+// move 256 contiguous bytes of each of 4 rows (DRAM sees 256-byte runs instead of 64-byte ones), each
+// wave owning 32 columns over the whole chunk.
 // fp32 mode (a debug mode) computes each output directly on the vector ALUs.
 #include "mla_device.h"
 
@@ -150,6 +153,91 @@ __global__ __launch_bounds__(256) void dense_proj_kernel(const uint16_t* __restr
   }
 }
 
+#ifndef MLA_OP4_CHUNK
+#define MLA_OP4_CHUNK 1024
+#endif
+constexpr int kChunk4 = MLA_OP4_CHUNK;   // weight rows per workgroup (wide form)
+constexpr int kSlab4 = 128;              // weight rows per slab (wide form)
+constexpr int kRow4 = 256;               // slab row bytes: 128 columns
+
+// Wide form for batches up to 32: workgroup (K chunk, 128-column block); each copy moves 4 rows x
+// 256 contiguous bytes (16-byte unit u of slab row r stored at unit u ^ 2 (r mod 4), so that the
+// four rows of a transposing read fall on different banks); wave w owns columns 32 w .. 32 w + 31
+// over the whole chunk, so no K halves are summed.  part[kc][b][n], as the narrow form.
+__global__ __launch_bounds__(256) void dense_proj4_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w, int K,
+                                                          float* __restrict__ part, int batch) {
+  __shared__ __attribute__((aligned(1024))) char slab[2][kSlab4 * kRow4];
+  const int kc = blockIdx.x;
+  const int n0 = blockIdx.y * 128;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const uint16_t* wk = w + (size_t)kc * kChunk4 * kN + n0;
+  constexpr int kCopies = kSlab4 * kRow4 / 1024 / 4;   // per wave and slab (8)
+  constexpr int kSteps4 = kSlab4 / 16;                 // k-steps per slab (8)
+  auto swz = [](int r) { return 2 * (r & 3); };
+  auto issue_slab = [&](int s, int buf) __attribute__((always_inline)) {
+    const unsigned lds0 = (unsigned)(uintptr_t)(LDS_AS char*)&slab[buf][0];
+#pragma unroll
+    for (int jj = 0; jj < kCopies; ++jj) {
+      const int j = wave + 4 * jj;
+      const int r = 4 * j + lane / 16;
+      const int u = (lane % 16) ^ swz(r);
+      dma16(wk + (size_t)(kSlab4 * s + r) * kN + 8 * u, lds0 + j * 1024);
+    }
+  };
+  unsigned tr_off[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int r = 8 * half + ((lane & 15) >> 2) + 4 * rd;
+    const int u = 4 * wave + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tr_off[rd] = (unsigned)(r * kRow4 + 16 * (u ^ swz(r)) + 8 * (lane & 1));
+  }
+  constexpr int kSlabs4 = kChunk4 / kSlab4;
+  f32x16 acc = {};
+  bf16x8 a_cur[kSteps4], a_nxt[kSteps4];
+  const int row = min(lane & 31, batch - 1);   // rows past the batch repeat the last (never stored)
+  auto load_a = [&](int s, bf16x8 (&a)[kSteps4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kSteps4; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(x + (size_t)row * K + kc * kChunk4 + kSlab4 * s + 16 * i + 8 * half);
+  };
+  issue_slab(0, 0);
+  load_a(0, a_cur);
+#pragma unroll 1
+  for (int s = 0; s < kSlabs4; ++s) {
+    if (s + 1 < kSlabs4) {
+      issue_slab(s + 1, (s + 1) & 1);
+      load_a(s + 1, a_nxt);
+      wait_vmcnt<kCopies + kSteps4>();   // slab s (and its rows) have landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const unsigned base = (unsigned)(uintptr_t)(LDS_AS char*)&slab[s & 1][0];
+#pragma unroll
+    for (int i = 0; i < kSteps4; ++i) {
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)((LDS_AS char*)(uintptr_t)(base + tr_off[0]) + i * 16 * kRow4));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)((LDS_AS char*)(uintptr_t)(base + tr_off[1]) + i * 16 * kRow4));
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur[i], bop, acc, 0, 0, 0);
+    }
+    __syncthreads();  // every wave is done with this buffer before slab s + 2 refills it
+    if (s + 1 < kSlabs4) {
+#pragma unroll
+      for (int i = 0; i < kSteps4; ++i) a_cur[i] = a_nxt[i];
+    }
+  }
+  // acc lane l, register j: row 8 (j / 4) + 4 half + j % 4, column l % 32 of the wave's block
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 8 * (j >> 2) + 4 * half + (j & 3);
+    if (r < batch) part[((size_t)kc * batch + r) * kN + n0 + 32 * wave + (lane & 31)] = acc[j];
+  }
+}
+
 // hidden[b][n] = sum over chunks (in order) of part[c][b][n], rounded to bf16; 4 outputs a thread.
 __global__ __launch_bounds__(256) void dense_finish_kernel(const float* __restrict__ part, int chunks,
                                                            int batch, uint16_t* __restrict__ out) {
@@ -182,7 +270,8 @@ __global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict_
 }  // namespace
 
 size_t out_proj_hidden_workspace_bytes(int batch, int heads) {
-  return (size_t)(heads * kDv / kChunk) * (size_t)batch * kN * sizeof(float);
+  const int chunk = kChunk4 < kChunk ? kChunk4 : kChunk;   // the form with more partials
+  return (size_t)(heads * kDv / chunk) * (size_t)batch * kN * sizeof(float);
 }
 
 hipError_t launch_out_proj_hidden(const void* out, const void* w_o, void* hidden, int batch, int heads,
@@ -193,9 +282,13 @@ hipError_t launch_out_proj_hidden(const void* out, const void* w_o, void* hidden
                        (const float*)w_o, K, (float*)hidden);
     return hipGetLastError();
   }
-  const int chunks = K / kChunk;
+  int chunks = K / kChunk;
   const dim3 grid(chunks, kN / 64);
-  if (batch <= 32)
+  if (batch <= 32 && K % kChunk4 == 0) {
+    chunks = K / kChunk4;
+    hipLaunchKernelGGL(dense_proj4_kernel, dim3(chunks, kN / 128), dim3(256), 0, s, (const uint16_t*)out,
+                       (const uint16_t*)w_o, K, part, batch);
+  } else if (batch <= 32)
     hipLaunchKernelGGL(dense_proj_kernel<1>, grid, dim3(256), 0, s, (const uint16_t*)out, (const uint16_t*)w_o, K,
                        part, batch);
   else
