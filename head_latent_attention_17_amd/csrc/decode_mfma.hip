@@ -33,6 +33,8 @@
 // With it, the 16 lanes of one row read of the score operand (16 tokens, one chunk) and of one
 // transposing read (4 tokens x 2 chunks) always land on 16 different 16-byte bank groups.
 //
+// The file also holds the decode over the ~6-bit cache (decode_fp6_kernel, below): the same work
+// split, ring and softmax, with operands converted from the codes in registers.
 #include "mla_device.h"
 
 namespace mla {
@@ -912,6 +914,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_fp6_kernel(DecodeParams p) 
     const u32x3 c1 = *reinterpret_cast<const LDS_AS u32x3*>((const LDS_AS char*)(uintptr_t)((st + ko[j & 1] + 128 * (j >> 1)) ^ 16u));
     codes = u32x6{c0[0], c0[1], c0[2], c1[0], c1[1], c1[2]};
   };
+  // 32 codes -> 32 bf16 (times the exponent of sc).  Written as asm: the compiler's builtin for this
+  // conversion returned its first element in every position when probed on the GPU.
   auto cvt32 = [&](const u32x6& codes, float sc) __attribute__((always_inline)) {
     u32x16 v;
     asm volatile("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2" : "=&v"(v) : "v"(codes), "v"(sc));
