@@ -7,7 +7,8 @@
 // All heads of a sequence share every cached row (the row is per token, not per head), so heads
 // form the N dimension of both products and each row is read from HBM once per launch.
 //
-// Workgroup = 4 waves x 32 heads = 128 heads, one workgroup per compute unit.  Per 32-token tile:
+// Workgroup = 4 waves x 32 heads = 128 heads, one workgroup per compute unit (fewer heads: the
+// waves' columns repeat heads, see head_of).  Per 32-token tile:
 //   scores  S^T[t][h] = K . Q^T   M = 32 tokens, N = 32 heads, K = 576  (36 MFMAs per wave)
 //   output  O^T[d][h] = V^T . P^T M = 32 dims,   N = 32 heads, K = 32   (16 blocks x 2 MFMAs)
 // Q stays in VGPRs for a whole segment; O^T (32 x 512 fp32 per wave) stays in the 256 AGPRs.  The
@@ -445,9 +446,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   // The query of a segment lives in VGPRs for the whole segment (36 x 8 bf16 per lane).
   const uint16_t* qa = static_cast<const uint16_t*>(p.q_abs);
   bf16x8 q[36];
-  // Head of accumulator column c (0 .. 31) of this wave.  With 16 heads the columns 16 .. 31 repeat
-  // heads 0 .. 15: same query, same data, so bit-identical results, and every store they make
-  // writes the same bits to the same place as the real head's.  (Heads are powers of two.)
+  // Head of accumulator column c (0 .. 31) of this wave: (32 wave + c) mod H.  Below 32 NW heads
+  // the columns repeat heads: same query, same data, so bit-identical results, and every store they
+  // make writes the same bits to the same place as the first copy's.  (Heads are powers of two.)
   auto head_of = [&](int c) __attribute__((always_inline)) { return (wave * 32 + c) & (p.heads - 1); };
   auto load_q = [&](int b) __attribute__((always_inline)) {
     const int ln = lane_id();
@@ -1202,23 +1203,13 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  if (p.positions) {
-    switch (p.heads) {
-      case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, true>), dim3(p.num_units), dim3(256), 0, s, p); break;
-      case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, true>), dim3(p.num_units), dim3(128), 0, s, p); break;
-      case 32:
-      case 16: hipLaunchKernelGGL((decode_mfma_kernel<1, true>), dim3(p.num_units), dim3(64), 0, s, p); break;
-      default: return hipErrorNotSupported;
-    }
-    return hipGetLastError();
-  }
-  switch (p.heads) {
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<4, false>), dim3(p.num_units), dim3(256), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<2, false>), dim3(p.num_units), dim3(128), 0, s, p); break;
-    case 32:
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<1, false>), dim3(p.num_units), dim3(64), 0, s, p); break;
-    default: return hipErrorNotSupported;
-  }
+  if (!mfma_supported(p)) return hipErrorNotSupported;
+  // Every head count runs four waves: below 128 heads their columns repeat heads, which spreads the
+  // tile copies over four waves instead of leaving them to H / 32.
+  if (p.positions)
+    hipLaunchKernelGGL((decode_mfma_kernel<4, true>), dim3(p.num_units), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<4, false>), dim3(p.num_units), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
