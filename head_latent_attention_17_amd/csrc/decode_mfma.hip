@@ -179,18 +179,19 @@ __device__ __forceinline__ float sum_halves(float x) {
 // Every field is wave-uniform and lives in scalar registers.
 struct TileCursor {
   const int32_t* lens;
-  int pg0, pg1;   // the unit's global page range
+  int sh;         // the cut's grain: 1 << sh tokens (32 under the weighted cut, else 64, a page)
+  int pg0, pg1;   // the unit's global range, in grains
   int b;          // current sequence
-  int before;     // pages of sequences [0, b)
-  int len, np;    // tokens / pages of sequence b
+  int before;     // grains of sequences [0, b)
+  int len, np;    // tokens / grains of sequence b
   int t;          // first token of the current tile
   int t_end;      // end token of the current segment
   bool valid;
-  bool all_live;  // every unit holds at least one page
+  bool all_live;  // every unit holds at least one grain
 
   __device__ __forceinline__ void load_seq() {
     len = ld_const(lens, b);
-    np = (int)(((unsigned)max(len, 0) + kPage - 1) / kPage);
+    np = (int)(((unsigned)max(len, 0) + (1u << sh) - 1) >> sh);
   }
   // Sets t / t_end for sequence b, skipping sequences with no tokens.
   __device__ __forceinline__ void enter() {
@@ -200,44 +201,171 @@ struct TileCursor {
     }
     const int p0 = max(pg0 - before, 0);
     const int p1 = min(pg1 - before, np);
-    t = p0 * kPage;
-    t_end = min(p1 * kPage, len);
+    t = p0 << sh;
+    t_end = min(p1 << sh, len);
+  }
+  // a / d for a >= 0, d > 0: a 32-bit division when `small` (operands below 2^32), else 64-bit.
+  static __device__ __forceinline__ long long udiv(long long a, long long d, bool small) {
+    return small ? (long long)((unsigned)a / (unsigned)d) : a / d;
+  }
+  // Unit w's range from a batch of at most 64 NCH sequences held in registers (lane i of chunk c
+  // holds sequence 64 c + i): the cost-weighted tile cut with at least 8 tiles per unit (every unit
+  // then holds a tile), else the plain page cut [floor(w P / W), floor((w + 1) P / W)).
+  template <int NCH>
+  __device__ __forceinline__ void init_resident(const DecodeParams& p, int w) {
+    const int W = p.num_units;
+    const int ln = threadIdx.x & 63;
+    int len_c[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) len_c[c] = 64 * c + ln < p.batch ? max(p.seq_lens[64 * c + ln], 0) : 0;
+    // tiles per sequence, inclusive scans of tiles and of non-empty sequences across the chunks
+    int nt_c[NCH], tin_c[NCH], nc_c[NCH];
+    int tb = 0, nb = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      nt_c[c] = (len_c[c] + 31) >> 5;
+      int ti = nt_c[c], ni = nt_c[c] > 0 ? 1 : 0;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int n = __shfl_up(ti, o, 64);
+        const int m = __shfl_up(ni, o, 64);
+        if (ln >= o) {
+          ti += n;
+          ni += m;
+        }
+      }
+      tin_c[c] = tb + ti;
+      nc_c[c] = nb + ni;
+      tb = __builtin_amdgcn_readlane(tin_c[c], 63);
+      nb = __builtin_amdgcn_readlane(nc_c[c], 63);
+    }
+    const int T = tb;
+    int unit_incl[NCH], unit_n[NCH];  // the cut's grains per sequence and their inclusive scan
+    if (weighted_cut(T, W)) {
+      sh = 5;
+      const bool small = ((long long)T + (long long)kSegmentCostTiles * p.batch + 1) * W < (1LL << 32);
+      const long long cw = udiv((long long)w * T, W, small);
+      // walls around cw: the last at or before it (k0) and the first after it (k1)
+      int A0 = 0, n0 = 0, k0 = 0, A1 = T, n1 = nb, k1 = p.batch;
+      bool found1 = false;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int sl = tin_c[c] - nt_c[c];
+        const bool wall = nt_c[c] > 0 && udiv((udiv((long long)sl * W + T - 1, T, small)) * T, W, small) == sl;
+        const unsigned long long lo = __ballot(wall && sl <= cw);
+        const unsigned long long hi = __ballot(wall && sl > cw);
+        if (!found1 && lo) {
+          const int f = 63 - __clzll((long long)lo);
+          A0 = __builtin_amdgcn_readlane(sl, f);
+          n0 = __builtin_amdgcn_readlane(nc_c[c], f);
+          k0 = 64 * c + f;
+        }
+        if (!found1 && hi) {
+          const int f = __ffsll((long long)hi) - 1;
+          A1 = __builtin_amdgcn_readlane(sl, f);
+          n1 = __builtin_amdgcn_readlane(nc_c[c], f) - 1;
+          k1 = 64 * c + f;
+          found1 = true;
+        }
+      }
+      const long long wa0 = udiv((long long)A0 * W + T - 1, T, small);
+      const long long wa1 = found1 ? udiv((long long)A1 * W + T - 1, T, small) : W;
+      const long long V = (A1 - A0) + (long long)kSegmentCostTiles * (n1 - n0);
+      // the tile at virtual position x: the first sequence of the stretch whose tiles end past x
+      auto tile_at = [&](long long x) __attribute__((always_inline)) {
+        int r = A1;
+        bool done = x >= V;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const int sl = tin_c[c] - nt_c[c];
+          const int vs = sl - A0 + kSegmentCostTiles * (nc_c[c] - n0);  // virtual start of the lane's tiles
+          const int bi = 64 * c + ln;
+          const unsigned long long h = __ballot(!done && bi >= k0 && bi < k1 && nt_c[c] > 0 && vs + nt_c[c] > x);
+          if (h) {
+            const int f = __ffsll((long long)h) - 1;
+            r = __builtin_amdgcn_readlane(sl, f) + max((int)x - __builtin_amdgcn_readlane(vs, f), 0);
+            done = true;
+          }
+        }
+        return r;
+      };
+      pg0 = uni(tile_at(udiv((w - wa0) * V, wa1 - wa0, small)));
+      pg1 = uni(tile_at(udiv((w - wa0 + 1) * V, wa1 - wa0, small)));
+      all_live = true;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        unit_incl[c] = tin_c[c];
+        unit_n[c] = nt_c[c];
+      }
+    } else {
+      sh = 6;
+      int pb = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        unit_n[c] = (len_c[c] + kPage - 1) / kPage;
+        int pi = unit_n[c];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int n = __shfl_up(pi, o, 64);
+          if (ln >= o) pi += n;
+        }
+        unit_incl[c] = pb + pi;
+        pb = __builtin_amdgcn_readlane(unit_incl[c], 63);
+      }
+      const int P = pb;
+      pg0 = uni((int)((long long)w * P / W));
+      pg1 = uni((int)((long long)(w + 1) * P / W));
+      all_live = P >= W;
+    }
+    valid = pg0 < pg1;
+    if (!valid) return;
+    // the sequence holding the unit's first grain
+    bool found = false;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const unsigned long long h = __ballot(!found && 64 * c + ln < p.batch && unit_incl[c] > pg0);
+      if (h) {
+        const int f = __ffsll((long long)h) - 1;
+        b = 64 * c + f;
+        before = __builtin_amdgcn_readlane(unit_incl[c] - unit_n[c], f);
+        found = true;
+      }
+    }
+    b = uni(b);
+    before = uni(before);
   }
   __device__ __forceinline__ void init(const DecodeParams& p, int w) {
     lens = p.seq_lens;
+    const int W = p.num_units;
     if (p.batch <= 64) {
-      // One pass: lane i holds sequence i's page count, an inclusive scan gives both the total and
-      // the sequence holding the unit's first page.
-      const int ln = threadIdx.x & 63;
-      const int np_l = ln < p.batch ? (int)(((unsigned)max(p.seq_lens[ln], 0) + kPage - 1) / kPage) : 0;
-      int incl = np_l;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int n = __shfl_up(incl, o, 64);
-        if (ln >= o) incl += n;
-      }
-      const int P = __builtin_amdgcn_readlane(incl, 63);
-      pg0 = uni((int)((long long)w * P / p.num_units));
-      pg1 = uni((int)((long long)(w + 1) * P / p.num_units));
-      all_live = P >= p.num_units;
-      valid = pg0 < pg1;
-      if (!valid) return;
-      const unsigned long long hit = __ballot(ln < p.batch && incl > pg0);
-      b = uni(__ffsll((long long)hit) - 1);
-      before = __builtin_amdgcn_readlane(incl - np_l, b);
+      init_resident<1>(p, w);
+    } else if (p.batch <= 256) {
+      init_resident<4>(p, w);
     } else {
-      const int P = uni((int)total_pages(p.seq_lens, p.batch));
-      pg0 = uni((int)((long long)w * P / p.num_units));
-      pg1 = uni((int)((long long)(w + 1) * P / p.num_units));
-      all_live = P >= p.num_units;
+      const int T = uni((int)total_tiles(p.seq_lens, p.batch));
+      if (weighted_cut(T, W)) {
+        sh = 5;
+        long long t0, t1;
+        weighted_unit_range(p.seq_lens, p.batch, W, w, T, t0, t1);
+        pg0 = uni((int)t0);
+        pg1 = uni((int)t1);
+        all_live = true;
+      } else {
+        sh = 6;
+        const int P = uni((int)total_pages(p.seq_lens, p.batch));
+        pg0 = uni((int)((long long)w * P / W));
+        pg1 = uni((int)((long long)(w + 1) * P / W));
+        all_live = P >= W;
+      }
       valid = pg0 < pg1;
       if (!valid) return;
       int bb;
       long long bf;
-      locate_page(p.seq_lens, p.batch, pg0, bb, bf);
+      locate_unit(p.seq_lens, p.batch, pg0, sh, bb, bf);
       b = uni(bb);
       before = uni((int)bf);
     }
+    if (!valid) return;
     load_seq();
     enter();
   }

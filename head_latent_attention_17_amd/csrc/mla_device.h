@@ -55,9 +55,10 @@ __device__ __forceinline__ long long wave_incl_scan_i64(long long v) {
 
 // ---------------------------------------------------------------------------------------------
 // Work units.  The pages of all sequences, concatenated in sequence order, are cut into
-// `num_units` ranges [floor(w P / W), floor((w+1) P / W)), P = sum_b ceil(len_b / 64).  Every
-// wave of every workgroup derives the same boundaries from seq_lens alone, so no host sync and no
-// planning launch are needed.
+// `num_units` ranges [floor(w P / W), floor((w+1) P / W)), P = sum_b ceil(len_b / 64) (the vector-ALU
+// decode, and the matrix-core decode below 8 tiles per unit); with more tiles the matrix-core decode
+// cuts 32-token tiles by cost instead (below).  Every wave of every workgroup derives the same
+// boundaries from seq_lens alone, so no host sync and no planning launch are needed.
 // ---------------------------------------------------------------------------------------------
 
 __device__ __forceinline__ int pages_of(int len) { return (int)(((unsigned)max(len, 0) + kPage - 1) / kPage); }
@@ -104,6 +105,132 @@ __device__ __forceinline__ void locate_page(const int32_t* seq_lens, int batch, 
       const long long np_first = __shfl(np, first, 64);
       b_out = b0 + first;
       before_out = incl_first - np_first;
+      return;
+    }
+    base = __shfl(incl, 63, 64);
+  }
+  b_out = batch;
+  before_out = base;
+}
+
+// Cost-weighted cut (the matrix-core decode's units), in tiles of 32 tokens.  A wave that moves on
+// to another sequence inside its unit pays about five tiles for it: the new query queues behind the
+// copies in flight, the finished piece is stored, and the first tile's scores run on their own.
+// Walls: a sequence start that the plain cut floor(w T / W) already puts on a unit boundary costs
+// nothing extra and stays a boundary.  Between two walls, the units that the plain cut gives that
+// stretch cut it into equal lengths of a virtual line on which every other non-empty sequence
+// spans kSegmentCostTiles positions for its start, then one per tile; a cut at virtual position x
+// goes to the tile where x falls, or to the first tile of the sequence whose start positions hold
+// x.  Used with at least 8 tiles per unit: every unit then spans at least 7 virtual positions, more
+// than a start's cost, so it always holds a tile (and every cut stays inside its stretch).
+constexpr int kSegmentCostTiles = 5;
+__device__ __forceinline__ int tiles_of(int len) { return (int)(((unsigned)max(len, 0) + 31) / 32); }
+__device__ __forceinline__ bool weighted_cut(long long total_tiles, int num_units) {
+  return total_tiles >= 8LL * num_units;
+}
+// Whether tile position s is a boundary of the plain cut of T tiles into W units.
+__device__ __forceinline__ bool plain_boundary(long long s, long long T, int W) {
+  const long long w = (s * W + T - 1) / T;
+  return w * T / W == s;
+}
+// First unit of the plain cut that starts at or after tile s.
+__device__ __forceinline__ long long plain_unit_at(long long s, long long T, int W) { return (s * W + T - 1) / T; }
+
+// Total tiles of the batch (wave-uniform result).
+__device__ __forceinline__ long long total_tiles(const int32_t* seq_lens, int batch) {
+  const int lane = threadIdx.x & 63;
+  long long s = 0;
+  for (int b = lane; b < batch; b += 64) s += tiles_of(seq_lens[b]);
+  return wave_sum_i64(s);
+}
+
+// Unit w's tile range [t0, t1) under the weighted cut, for a batch of any size (wave-uniform).  Two
+// passes over seq_lens: the walls around the plain cut of unit w, then the tiles at its two cuts.
+__device__ __forceinline__ void weighted_unit_range(const int32_t* seq_lens, int batch, int W, int w,
+                                                    long long T, long long& t0, long long& t1) {
+  const int lane = threadIdx.x & 63;
+  const long long cw = (long long)w * T / W;
+  long long A0 = 0, A1 = T, n0 = 0, n1 = 0;  // walls; non-empty sequences up to A0's, before A1's
+  int k0 = 0, k1 = batch;
+  long long sbase = 0, nbase = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int b = b0 + lane;
+    const long long nt = b < batch ? tiles_of(seq_lens[b]) : 0;
+    const long long s = sbase + wave_incl_scan_i64(nt) - nt;
+    const long long nc = nbase + wave_incl_scan_i64(nt > 0 ? 1 : 0);
+    const bool wall = nt > 0 && plain_boundary(s, T, W);
+    const unsigned long long lo = __ballot(wall && s <= cw);
+    if (lo) {
+      const int f = 63 - __clzll((long long)lo);
+      A0 = __shfl(s, f, 64);
+      n0 = __shfl(nc, f, 64);
+      k0 = b0 + f;
+    }
+    const unsigned long long hi = __ballot(wall && s > cw);
+    sbase = __shfl(s + nt, 63, 64);
+    nbase = __shfl(nc, 63, 64);
+    if (hi) {
+      const int f = __ffsll((long long)hi) - 1;
+      A1 = __shfl(s, f, 64);
+      n1 = __shfl(nc, f, 64) - 1;
+      k1 = b0 + f;
+      break;
+    }
+  }
+  if (k1 == batch) n1 = nbase;
+  const long long wa0 = plain_unit_at(A0, T, W), wa1 = k1 < batch ? plain_unit_at(A1, T, W) : W;
+  const long long V = (A1 - A0) + kSegmentCostTiles * (n1 - n0);
+  const long long x0 = (w - wa0) * V / (wa1 - wa0), x1 = (w - wa0 + 1) * V / (wa1 - wa0);
+  t0 = A1;
+  t1 = A1;
+  bool need0 = x0 < V, need1 = x1 < V;
+  sbase = 0;
+  nbase = 0;
+  for (int b0 = 0; b0 < k1 && (need0 || need1); b0 += 64) {
+    const int b = b0 + lane;
+    const long long nt = b < batch ? tiles_of(seq_lens[b]) : 0;
+    const long long s = sbase + wave_incl_scan_i64(nt) - nt;
+    const long long nc = nbase + wave_incl_scan_i64(nt > 0 ? 1 : 0);
+    const long long vs = s - A0 + kSegmentCostTiles * (nc - n0);  // virtual start of b's tiles
+    const bool in = b >= k0 && b < k1 && nt > 0;
+    if (need0) {
+      const unsigned long long h = __ballot(in && vs + nt > x0);
+      if (h) {
+        const int f = __ffsll((long long)h) - 1;
+        const long long d = x0 - __shfl(vs, f, 64);
+        t0 = __shfl(s, f, 64) + (d > 0 ? d : 0);
+        need0 = false;
+      }
+    }
+    if (need1) {
+      const unsigned long long h = __ballot(in && vs + nt > x1);
+      if (h) {
+        const int f = __ffsll((long long)h) - 1;
+        const long long d = x1 - __shfl(vs, f, 64);
+        t1 = __shfl(s, f, 64) + (d > 0 ? d : 0);
+        need1 = false;
+      }
+    }
+    sbase = __shfl(s + nt, 63, 64);
+    nbase = __shfl(nc, 63, 64);
+  }
+}
+
+// First sequence whose `1 << sh`-token units reach past global unit `p`, and the units before it
+// (wave-uniform).  Requires p < the batch's total.
+__device__ __forceinline__ void locate_unit(const int32_t* seq_lens, int batch, long long p, int sh,
+                                            int& b_out, long long& before_out) {
+  const int lane = threadIdx.x & 63;
+  long long base = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int b = b0 + lane;
+    const long long np = (b < batch) ? (long long)(((unsigned)max(seq_lens[b], 0) + (1u << sh) - 1) >> sh) : 0;
+    const long long incl = base + wave_incl_scan_i64(np);
+    const unsigned long long hit = __ballot(b < batch && incl > p);
+    if (hit) {
+      const int first = __ffsll((long long)hit) - 1;
+      b_out = b0 + first;
+      before_out = __shfl(incl, first, 64) - __shfl(np, first, 64);
       return;
     }
     base = __shfl(incl, 63, 64);
