@@ -74,6 +74,38 @@ def test_split_count_invariance(lib, splits):
     assert lse_err(g.lse.cpu().numpy()[:, hs], lse_ref[:, hs]) <= BF16_TOL
 
 
+@pytest.mark.parametrize("splits", [0, 97])
+def test_many_sequences_cost_weighted_cut(lib, splits):
+    """300 sequences of mixed lengths, every 23rd empty, with at least 8 tiles per unit: the units
+    are cut by cost over 32-token tiles, in passes over the lengths 64 sequences at a time (more
+    than 256 sequences).  Every sequence must still be covered exactly once by its pieces: sampled
+    sequences against the oracle, the empty ones exactly zero with lse -inf."""
+    rng = np.random.default_rng(303)
+    lens = [int(x) for x in rng.integers(1, 1200, 300)]
+    for i in range(0, len(lens), 23):
+        lens[i] = 0
+    wl = synth.make_custom(lens, heads=128, seed=303)
+    tiles = sum((n + 31) // 32 for n in lens)
+    units = splits or min(256, wl.batch * wl.max_blocks)
+    assert tiles >= 8 * units, "the workload must take the cost-weighted cut"
+    say("many sequences", wl.batch, "tiles", tiles, "units", units)
+    g = Gpu(wl)
+    g.step(lib, splits=splits, q_abs_from_absorb=False)
+    torch.cuda.synchronize()
+    sel = [b for b in sorted(set(range(1, wl.batch, 11)) | {wl.batch - 1}) if lens[b] > 0]
+    hs = list(range(0, 128, 9))
+    hi = host_inputs(wl, 0, sel)
+    o_ref, lse_ref = O.latent_decode_batch(hi["q_lat"], hi["cache"], wl.block_table, wl.attended_lens,
+                                           wl.scale, batch=sel, heads=hs)
+    o = to_host_f64(g.o_lat)
+    e = rel_err(o[sel][:, hs], o_ref[sel][:, hs])
+    e_l = lse_err(g.lse.cpu().numpy()[sel][:, hs], lse_ref[sel][:, hs])
+    say(f"  err {e:.3e}  lse err {e_l:.3e}")
+    assert e <= BF16_TOL and e_l <= BF16_TOL
+    empty = [b for b in range(wl.batch) if lens[b] == 0]
+    assert np.all(o[empty] == 0) and torch.all(torch.isneginf(g.lse[empty]))
+
+
 @pytest.mark.parametrize("f32", [False, True])
 def test_end_to_end_with_append_matches_decompressed_oracle(lib, f32):
     wl = synth.make_custom([1, 64, 200, 777], heads=128, seed=51, append=True)
