@@ -87,8 +87,10 @@ int mla_abi_version(void);
 
 /*
  * Bytes of workspace mla_decode needs for these sizes (0 on invalid arguments).
- * num_splits is the number of equal page ranges the batch's pages are cut into (0 = automatic: the
- * value mla_decode would choose).  The result does not depend on the sequence lengths.
+ * num_splits is the number of work units the batch's tokens are cut into (0 = automatic: the value
+ * mla_decode would choose): equal page ranges, or with at least 8 tiles of 32 tokens per unit, tile
+ * ranges cut so that a unit that starts another sequence holds fewer tiles.  The result does not
+ * depend on the sequence lengths.
  */
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype);
@@ -142,8 +144,9 @@ mla_status mla_absorb_q(const void* q, const void* w_uk, void* q_abs, int batch,
  *   s_t   = softmax_scale * (q_abs[b][h] . row_t),  t = 0 .. seq_lens[b]-1   (576-long dot)
  *   o_lat = sum_t softmax(s)_t * c_t                                          (512 wide)
  *   lse   = log sum_t exp(s_t)                                                (natural log)
- * The pages of all sequences are cut into num_splits equal ranges (0 = automatic); each range is
- * reduced by one workgroup and sequences cut across ranges are combined with a log-sum-exp merge.
+ * The tokens of all sequences are cut into num_splits ranges (0 = automatic; the cut is described at
+ * mla_decode_workspace_size); each range is reduced by one workgroup and sequences cut across
+ * ranges are combined with a log-sum-exp merge.
  * Results do not depend on num_splits beyond rounding; equal arguments give bit-identical results.
  * A sequence of length 0 gives o_lat = 0 and lse = -inf.  lse may be null.
  * workspace must hold mla_decode_workspace_size(batch, num_heads, max_blocks_per_seq, num_splits,
