@@ -157,11 +157,18 @@ __global__ __launch_bounds__(256) void dense_proj_kernel(const uint16_t* __restr
 #define MLA_OP4_CHUNK 1024
 #endif
 constexpr int kChunk4 = MLA_OP4_CHUNK;   // weight rows per workgroup (wide form)
-constexpr int kSlab4 = 128;              // weight rows per slab (wide form)
+// 32-row slabs (16 KB of LDS a workgroup with both buffers) let every workgroup of the grid be
+// resident at once: 45.6 against 54.0 us at batch 32 and 40.2 against 44.1 us at batch 4 with
+// 128-row slabs (64 KB, two workgroups a compute unit, so the grid's last fifth ran as a second
+// round); 16-row slabs spend more on barriers than they gain (60.5 us).
+#ifndef MLA_OP4_SLAB
+#define MLA_OP4_SLAB 32
+#endif
+constexpr int kSlab4 = MLA_OP4_SLAB;     // weight rows per slab (wide form)
 constexpr int kRow4 = 256;               // slab row bytes: 128 columns
 
-// Wide form for batches up to 32: workgroup (K chunk, 128-column block); each copy moves 4 rows x
-// 256 contiguous bytes (16-byte unit u of slab row r stored at unit u ^ 2 (r mod 4), so that the
+// Wide form for batches up to 32: workgroup (K chunk, 128-column block), the chunk walked in slabs
+// of kSlab4 rows, double-buffered; each copy moves 4 rows x 256 contiguous bytes (16-byte unit u of slab row r stored at unit u ^ 2 (r mod 4), so that the
 // four rows of a transposing read fall on different banks); wave w owns columns 32 w .. 32 w + 31
 // over the whole chunk, so no K halves are summed.  part[kc][b][n], as the narrow form.
 __global__ __launch_bounds__(256) void dense_proj4_kernel(const uint16_t* __restrict__ x,
@@ -175,8 +182,9 @@ __global__ __launch_bounds__(256) void dense_proj4_kernel(const uint16_t* __rest
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const uint16_t* wk = w + (size_t)kc * kChunk4 * kN + n0;
-  constexpr int kCopies = kSlab4 * kRow4 / 1024 / 4;   // per wave and slab (8)
-  constexpr int kSteps4 = kSlab4 / 16;                 // k-steps per slab (8)
+  constexpr int kCopies = kSlab4 * kRow4 / 1024 / 4;   // per wave and slab
+  constexpr int kSteps4 = kSlab4 / 16;                 // k-steps per slab
+  static_assert(kCopies >= 1 && kChunk4 % kSlab4 == 0, "whole copies per wave, whole slabs per chunk");
   auto swz = [](int r) { return 2 * (r & 3); };
   auto issue_slab = [&](int s, int buf) __attribute__((always_inline)) {
     const unsigned lds0 = (unsigned)(uintptr_t)(LDS_AS char*)&slab[buf][0];
