@@ -59,6 +59,7 @@ constexpr int kTileTok = 32;
 constexpr int kChunks = kRow / 8;                    // 72 16-byte chunks per row
 constexpr int kCG = kChunks / 8;                     // 9 chunk groups
 constexpr int kBlocks = kTileTok / 8 * kCG;          // 36 blocks of 8 tokens x 8 chunks
+constexpr int kWaves = 4;                            // waves of the bf16 kernel, 32 heads each
 constexpr int kTileBytes = kBlocks * 1024;           // 36,864
 constexpr int kStages = 4;                           // tiles it .. it+3
 static_assert((kStages & (kStages - 1)) == 0, "stage index by mask");
@@ -457,10 +458,10 @@ __device__ __forceinline__ uint64_t topk_row_addr(const DecodeParams& p, const T
 // DMA of one tile: wave w fills blocks [w * per, (w + 1) * per).  For a full tile the per-lane part
 // of every source address is one of two lane constants (token-group parity); a ragged tile (fewer
 // than 32 tokens) re-reads its last valid row in place of the missing ones.
-template <int NW, bool TOPK>
+template <bool TOPK>
 __device__ __forceinline__ void issue_tile(const DecodeParams& p, const TileCursor& c,
                                            LDS_AS char* stage, int wave) {
-  constexpr int kPer = kBlocks / NW;
+  constexpr int kPer = kBlocks / kWaves;
   const int nt = min(kTileTok, c.t_end - c.t);
   const unsigned lds = (unsigned)(uintptr_t)stage;
   int ln;
@@ -488,18 +489,10 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, const TileCurs
       const int tl = (ln >> 3) ^ par;
       lane_off[par] = tl * (kRow * 2) + ((ln & 7) ^ sigma(tl)) * 16;
     }
-    if constexpr (NW == 4) {  // wave w copies token group w
-      const char* gb = base + wave * 8 * (kRow * 2);
+    // wave w copies token group w
+    const char* gb = base + wave * 8 * (kRow * 2);
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) dma16_group(gb, (unsigned)lane_off[wave & 1], lds + wave * kPer * 1024, j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int blk = wave * kPer + j;
-        const int tg = blk / kCG, cg = blk % kCG;
-        dma16(base + tg * 8 * (kRow * 2) + cg * 128, (unsigned)lane_off[tg & 1], lds + blk * 1024);
-      }
-    }
+    for (int j = 0; j < kPer; ++j) dma16_group(gb, (unsigned)lane_off[wave & 1], lds + wave * kPer * 1024, j);
   } else {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -544,13 +537,13 @@ __device__ __forceinline__ int xcd_unit(int id, int n) {
   return x * per + min(x, rem) + id / 8;
 }
 
-template <int NW, bool TOPK>
-__global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p) {
-  constexpr int kPer = kBlocks / NW;  // copies per wave per tile
+template <bool TOPK>
+__global__ __launch_bounds__(kWaves * 64, 1) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int kPer = kBlocks / kWaves;  // copies per wave per tile
   __shared__ __attribute__((aligned(1024))) char ring[kStages][kTileBytes];
-  // Target of the copies a four-wave unit issues after its last tile: they keep the count of copies
-  // per tile fixed, which the counted waits rely on, and nothing reads them.
-  __shared__ __attribute__((aligned(1024))) char sink[NW == 4 ? kPer * 1024 : 16];
+  // Target of the copies a unit issues after its last tile: they keep the count of copies per tile
+  // fixed, which the counted waits rely on, and nothing reads them.
+  __shared__ __attribute__((aligned(1024))) char sink[kPer * 1024];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -574,7 +567,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
   // The query of a segment lives in VGPRs for the whole segment (36 x 8 bf16 per lane).
   const uint16_t* qa = static_cast<const uint16_t*>(p.q_abs);
   bf16x8 q[36];
-  // Head of accumulator column c (0 .. 31) of this wave: (32 wave + c) mod H.  Below 32 NW heads
+  // Head of accumulator column c (0 .. 31) of this wave: (32 wave + c) mod H.  Below 128 heads
   // the columns repeat heads: same query, same data, so bit-identical results, and every store they
   // make writes the same bits to the same place as the first copy's.  (Heads are powers of two.)
   auto head_of = [&](int c) __attribute__((always_inline)) { return (wave * 32 + c) & (p.heads - 1); };
@@ -593,7 +586,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s) {
     if (ld.valid) {
-      issue_tile<NW, TOPK>(p, ld, (LDS_AS char*)ring[s], wave);
+      issue_tile<TOPK>(p, ld, (LDS_AS char*)ring[s], wave);
       ld.advance();
       ++issued;
     }
@@ -612,14 +605,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
     else if (younger == 1) wait_vmcnt<(kPer < 63 ? kPer : 63)>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-  };
-  // Refills the stage of the tile before `t` (every wave is past it) with the next tile.
-  auto refill = [&](int t) __attribute__((always_inline)) {
-    if (ld.valid) {
-      issue_tile<NW, TOPK>(p, ld, (LDS_AS char*)ring[stage_of(t + kStages - 1)], wave);
-      ld.advance();
-      ++issued;
-    }
   };
 
   // Scores of a ragged tile (n < 32 tokens) with the tokens past the end at -inf, so that they take
@@ -695,7 +680,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       uint64_t sp_addr = 0;  // kept tokens: this lane's full source address
       int sp_page = 0, sp_tok = 0;
       bool sp_have = false;
-      if constexpr (NW == 4) {
+      {
         const int ln = lane_id();
         const int tl = (ln >> 3) ^ (wave & 1);
         const unsigned cl16 = (unsigned)((ln & 7) ^ sigma(tl)) * 16u;
@@ -720,19 +705,16 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeParams p)
       // The next tile must be in LDS before its scores start; the barrier also frees the stage of
       // tile it - 1.
       tile_ready(last ? it : it + 1);
-      if constexpr (NW == 4 && TOPK) {
-        ++issued;
+      ++issued;
+      if constexpr (TOPK) {
         asm volatile("" : "+v"(sp_addr));
-      } else if constexpr (NW == 4) {
-        ++issued;
+      } else {
         asm volatile("" : "+s"(sp_page));  // the page is first needed here, behind the wait
         if (sp_have) sp_base += ((size_t)sp_page * kPage + sp_tok) * (kRow * 2);
-      } else {
-        refill(it);
       }
       auto spread_copy = [&](int j) __attribute__((always_inline)) {
-        if constexpr (NW == 4 && TOPK) dma16_addr(sp_addr, sp_lds + 1024 * j, j);
-        else if constexpr (NW == 4) dma16_group(sp_base, sp_lane, sp_lds, j);
+        if constexpr (TOPK) dma16_addr(sp_addr, sp_lds + 1024 * j, j);
+        else dma16_group(sp_base, sp_lane, sp_lds, j);
       };
 
       // ---- softmax of tile it (base 2), lane = head, registers = tokens, spread over the next
@@ -1335,9 +1317,9 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
   // Every head count runs four waves: below 128 heads their columns repeat heads, which spreads the
   // tile copies over four waves instead of leaving them to H / 32.
   if (p.positions)
-    hipLaunchKernelGGL((decode_mfma_kernel<4, true>), dim3(p.num_units), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<true>), dim3(p.num_units), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<4, false>), dim3(p.num_units), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<false>), dim3(p.num_units), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
