@@ -252,10 +252,20 @@ __global__ __launch_bounds__(256) void dense_finish_kernel(const float* __restri
   const int b = blockIdx.y;
   const int n = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (n >= kN) return;
-  float4 s = *reinterpret_cast<const float4*>(part + (size_t)b * kN + n);
-  for (int c = 1; c < chunks; ++c) {
-    const float4 v = *reinterpret_cast<const float4*>(part + ((size_t)c * batch + b) * kN + n);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  // The partials' loads go out eight at a time before any is added (the sum still runs in chunk
+  // order), instead of one memory round trip per chunk.
+  constexpr int kGroup = 8;
+  float4 s = make_float4(-0.f, -0.f, -0.f, -0.f);   // -0 + x is x for every x
+  for (int c0 = 0; c0 < chunks; c0 += kGroup) {
+    float4 v[kGroup];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u)
+      if (c0 + u < chunks) v[u] = *reinterpret_cast<const float4*>(part + ((size_t)(c0 + u) * batch + b) * kN + n);
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u)
+      if (c0 + u < chunks) {
+        s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+      }
   }
   uint2 packed;
   packed.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
