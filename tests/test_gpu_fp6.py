@@ -111,7 +111,12 @@ def _decode_case(lib, wl, splits=0, seqs=None, heads=None):
     g = Gpu(wl)
     seqs = list(range(wl.batch)) if seqs is None else seqs
     hi = host_inputs(wl, 0, seqs)
-    pages6 = O.quantize_pages_fp6(hi["cache"])
+    # Pages outside the selected sequences are zero; a zero page always quantizes to the same bytes,
+    # so only the others go through the quantizer (the same pages as quantizing all of them).
+    cache = hi["cache"]
+    nz = np.flatnonzero(cache.reshape(cache.shape[0], -1).any(axis=1))
+    pages6 = np.repeat(O.quantize_pages_fp6(np.zeros((1,) + cache.shape[1:], cache.dtype)), cache.shape[0], axis=0)
+    pages6[nz] = O.quantize_pages_fp6(cache[nz])
     cache6 = _to_dev(pages6)
     lib.mla_decode_fp6(g.q_lat_in, cache6, g.bt, g.attended, wl.scale, g.o_lat, g.lse,
                        g.workspace(lib, splits), splits)
@@ -144,6 +149,24 @@ def test_split_counts(lib, splits):
     e_o, e_l, _ = _decode_case(lib, wl, splits=splits, heads=list(range(0, 128, 9)))
     say(f"  o_lat err {e_o:.3e}  lse err {e_l:.3e}")
     assert e_o <= BF16_TOL and e_l <= BF16_TOL
+
+
+def test_many_sequences_cost_weighted_cut(lib):
+    """300 sequences (every 23rd empty) with at least 8 tiles per unit: the ~6-bit kernel's units
+    come from the cost-weighted cut's passes over the lengths, 64 sequences at a time."""
+    rng = np.random.default_rng(304)
+    lens = [int(x) for x in rng.integers(1, 1200, 300)]
+    for i in range(0, len(lens), 23):
+        lens[i] = 0
+    wl = synth.make_custom(lens, heads=128, seed=304)
+    assert sum((n + 31) // 32 for n in lens) >= 8 * min(256, wl.batch * wl.max_blocks)
+    say("decode fp6, 300 sequences")
+    seqs = [b for b in sorted(set(range(1, wl.batch, 13)) | {wl.batch - 1}) if lens[b] > 0]
+    e_o, e_l, g = _decode_case(lib, wl, seqs=seqs, heads=list(range(0, 128, 9)))
+    say(f"  o_lat err {e_o:.3e}  lse err {e_l:.3e}")
+    assert e_o <= BF16_TOL and e_l <= BF16_TOL
+    empty = [b for b in range(wl.batch) if lens[b] == 0]
+    assert torch.all(g.o_lat[empty].float() == 0) and torch.all(torch.isneginf(g.lse[empty]))
 
 
 def test_empty_sequences(lib):
