@@ -762,18 +762,22 @@ def main():
         for _ in range(args.steps):
             lib.mla_decode_out_proj(res.q_abs, d["cache"], res.bt, res.att, wl.scale, d["w_uv"], res.out, None,
                                     None, res.ws, res.splits)
-        c6 = torch.empty((d["cache"].shape[0], lib.FP6_PAGE_BYTES), dtype=torch.uint8, device=dev)
-        lib.mla_cache_quantize_fp6(d["cache"], c6)
-        for _ in range(args.steps):
-            lib.mla_decode_fp6(res.q_abs, c6, res.bt, res.att, wl.scale, res.o_lat, res.lse, res.ws, res.splits)
+        fp6 = wl.heads in (64, 128)     # the ~6-bit cache path takes 64 or 128 heads only
+        if fp6:
+            c6 = torch.empty((d["cache"].shape[0], lib.FP6_PAGE_BYTES), dtype=torch.uint8, device=dev)
+            lib.mla_cache_quantize_fp6(d["cache"], c6)
+            for _ in range(args.steps):
+                lib.mla_decode_fp6(res.q_abs, c6, res.bt, res.att, wl.scale, res.o_lat, res.lse, res.ws,
+                                   res.splits)
+            del c6
         torch.cuda.synchronize()
-        del res, c6
+        del res
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        say(f"profile run done: {args.steps} mla_decode, mla_decode_out_proj and mla_decode_fp6 calls, one "
-            f"{CALIB_BYTES} B copy")
+        say(f"profile run done: {args.steps} mla_decode and mla_decode_out_proj calls"
+            f"{', ' + str(args.steps) + ' mla_decode_fp6 calls' if fp6 else ''}, one {CALIB_BYTES} B copy")
         return
 
     main_rec = time_workload(lib, res, args.steps, args.warmup)
