@@ -115,16 +115,28 @@ __global__ __launch_bounds__(256) void index_score_kernel(const int8_t* __restri
   }
 }
 
+// Inclusive scan over the 64 lanes of a wave (every lane active): within each row of 16 lanes by
+// data-parallel moves (row_shr 1, 2, 4, 8; lanes shifted in from outside the row read 0), then
+// each row adds the totals of the rows below it, read from lanes 15, 31 and 47.  Register moves
+// only, where a shuffle would make six round trips through the LDS crossbar.
+__device__ __forceinline__ int wave_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
 // Inclusive scan over a workgroup of NT threads (one value each) through the wave totals in LDS;
 // the workgroup total goes to *total.
 template <int NT>
 __device__ __forceinline__ int block_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+  v = wave_scan(v);
   if (lane == 63) wsum[wave] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -236,48 +248,53 @@ __global__ __launch_bounds__(256) void topk_count_kernel(const int32_t* __restri
   }
 }
 
-// Writes the kept positions of chunk blockIdx.x in increasing order.  Its output offset is the
-// number of kept keys in the earlier chunks: all their keys above T, plus min(keys equal to T that
-// are kept, keys equal to T in them), since the equal keys are kept in position order.
+// Writes the kept positions of chunk blockIdx.x in increasing order.  The kept keys before a
+// position are all the keys above T before it plus min(need_eq, keys equal to T before it), since
+// the equal keys are kept in position order; the earlier chunks' two counts are summed, and one scan
+// of the pair (above T, equal to T) inside the chunk (each at most 1,024: they share one int) adds
+// the rest.
 __global__ __launch_bounds__(kChunk) void topk_write_kernel(const int32_t* __restrict__ seq_lens, int k, TopkWs w,
                                                             int32_t* __restrict__ positions,
                                                             int32_t* __restrict__ counts) {
   __shared__ int wsum[kChunk / 64];
-  __shared__ int tot[2];
+  __shared__ int red[2][kChunk / 64];
+  __shared__ int tot[1];
   const int b = blockIdx.y;
   const int c = blockIdx.x;
   const int len = max(seq_lens[b], 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (c == 0 && threadIdx.x == 0) counts[b] = min(len, k);
   if (c * kChunk >= len) return;
   const int T = w.pick[4 * b + 2], need_eq = w.pick[4 * b + 3];
-  int gt_before = 0, eq_before = 0;
-  for (int c0 = 0; c0 < c; c0 += kChunk) {
-    const int cc = c0 + threadIdx.x;
-    int g = 0, e = 0;
-    if (cc < c) {
-      const int32_t* ch = w.chunk + ((size_t)b * w.nchunks + cc) * 2;
-      g = ch[0];
-      e = ch[1];
-    }
-    block_scan<kChunk>(g, wsum, &tot[0]);
-    gt_before += tot[0];
-    block_scan<kChunk>(e, wsum, &tot[1]);
-    eq_before += tot[1];
+  int g = 0, e = 0;
+  for (int cc = threadIdx.x; cc < c; cc += kChunk) {
+    const int32_t* ch = w.chunk + ((size_t)b * w.nchunks + cc) * 2;
+    g += ch[0];
+    e += ch[1];
   }
-  const int base = gt_before + min(need_eq, eq_before);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    g += __shfl_xor(g, o, 64);
+    e += __shfl_xor(e, o, 64);
+  }
+  if (lane == 0) { red[0][wave] = g; red[1][wave] = e; }
   const int t = c * kChunk + threadIdx.x;
   const int key = t < len ? (T < 0 ? 1 : key_of(w.scores[(size_t)b * w.stride + t])) : -2;
-  const int eq = (t < len && key == T) ? 1 : 0;
-  const int eq_rank = eq_before + block_scan<kChunk>(eq, wsum, &tot[0]) - 1;
-  const int take = (t < len && (key > T || (eq && eq_rank < need_eq))) ? 1 : 0;
-  const int at = base + block_scan<kChunk>(take, wsum, &tot[1]) - 1;
+  const int pair = (key > T ? 1 : 0) | (key == T ? 1 << 16 : 0);
+  const int before = block_scan<kChunk>(pair, wsum, &tot[0]) - pair;  // its barriers publish red too
+  int gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int i = 0; i < kChunk / 64; ++i) { gt_before += red[0][i]; eq_before += red[1][i]; }
+  const int eq_rank = eq_before + (before >> 16);
+  const int take = key > T || (key == T && eq_rank < need_eq);
+  const int at = gt_before + (before & 0xffff) + min(need_eq, eq_rank);
   if (take) positions[(size_t)b * k + at] = t;
 }
 
 // The selection for one sequence in one workgroup, for block tables of at most kSmallMax tokens:
 // its scores (written by the scoring kernel) are staged in LDS, both radix passes count in LDS, and
 // the kept positions are written in increasing order (each thread owns a run of consecutive
-// positions; two scans place the runs).  Same result as the multi-workgroup passes: the k highest keys, ties to the earlier
+// positions; one scan places the runs).  Same result as the multi-workgroup passes: the k highest keys, ties to the earlier
 // position.
 __global__ __launch_bounds__(kSmallThreads) void topk_select_small_kernel(const int32_t* __restrict__ seq_lens,
                                                                          int k, TopkWs w,
@@ -286,7 +303,7 @@ __global__ __launch_bounds__(kSmallThreads) void topk_select_small_kernel(const 
   __shared__ int32_t sc[kSmallMax];
   __shared__ int32_t hist[kBins1];
   __shared__ int wsum[kSmallThreads / 64];
-  __shared__ int tot[2];
+  __shared__ int tot[1];
   __shared__ int d_s, left_s;
   const int b = blockIdx.x;
   const int len = max(seq_lens[b], 0);
@@ -330,25 +347,29 @@ __global__ __launch_bounds__(kSmallThreads) void topk_select_small_kernel(const 
   pick_bin<kBins2, kSmallThreads>(hist, left1, &d_s, &left_s);
   __syncthreads();
   const int T = (d1 << 11) | d_s, need_eq = left_s;
-  // Thread i owns the J consecutive positions from J i: one scan of the keys equal to T (those kept
-  // are the first need_eq of them), one of the kept positions, then each thread writes its own.
+  // Thread i owns the J consecutive positions from J i, its keys held in registers (-1 where there
+  // is no token: below every key).  The keys kept before its run are those above T plus the first
+  // need_eq keys equal to T in position order, so one scan of the pair (above T, equal to T) places
+  // every run: start = above + min(need_eq, equal).  Both counts are at most 2^14 and share one int.
+  constexpr int kJ = kSmallMax / kSmallThreads;
   const int J = (len + kSmallThreads - 1) / kSmallThreads;
   const int t0 = tid * J, t1 = min(t0 + J, len);
-  int eq_mine = 0;
-  for (int t = t0; t < t1; ++t) eq_mine += key_of(sc[t]) == T;
-  int eq_rank = block_scan<kSmallThreads>(eq_mine, wsum, &tot[0]) - eq_mine;
-  int take_mine = 0;
-  for (int t = t0; t < t1; ++t) {
-    const int key = key_of(sc[t]);
-    take_mine += key > T || (key == T && eq_rank < need_eq);
-    eq_rank += key == T;
+  int key[kJ];
+  int gt_mine = 0, eq_mine = 0;
+#pragma unroll
+  for (int u = 0; u < kJ; ++u) {
+    key[u] = u < J && t0 + u < t1 ? key_of(sc[t0 + u]) : -1;
+    gt_mine += key[u] > T;
+    eq_mine += key[u] == T;
   }
-  int at = block_scan<kSmallThreads>(take_mine, wsum, &tot[1]) - take_mine;
-  eq_rank -= eq_mine;
-  for (int t = t0; t < t1; ++t) {
-    const int key = key_of(sc[t]);
-    if (key > T || (key == T && eq_rank < need_eq)) out[at++] = t;
-    eq_rank += key == T;
+  const int pair = gt_mine | (eq_mine << 16);
+  const int before = block_scan<kSmallThreads>(pair, wsum, &tot[0]) - pair;
+  int eq_rank = before >> 16;
+  int at = (before & 0xffff) + min(need_eq, eq_rank);
+#pragma unroll
+  for (int u = 0; u < kJ; ++u) {
+    if (key[u] > T || (key[u] == T && eq_rank < need_eq)) out[at++] = t0 + u;
+    eq_rank += key[u] == T;
   }
 }
 
