@@ -225,16 +225,7 @@ struct TileCursor {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       nt_c[c] = (len_c[c] + 31) >> 5;
-      int ti = nt_c[c], ni = nt_c[c] > 0 ? 1 : 0;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int n = __shfl_up(ti, o, 64);
-        const int m = __shfl_up(ni, o, 64);
-        if (ln >= o) {
-          ti += n;
-          ni += m;
-        }
-      }
+      const int ti = wave_incl_scan(nt_c[c]), ni = wave_incl_scan(nt_c[c] > 0 ? 1 : 0);
       tin_c[c] = tb + ti;
       nc_c[c] = nb + ni;
       tb = __builtin_amdgcn_readlane(tin_c[c], 63);
@@ -304,13 +295,7 @@ struct TileCursor {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         unit_n[c] = (len_c[c] + kPage - 1) / kPage;
-        int pi = unit_n[c];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int n = __shfl_up(pi, o, 64);
-          if (ln >= o) pi += n;
-        }
-        unit_incl[c] = pb + pi;
+        unit_incl[c] = pb + wave_incl_scan(unit_n[c]);
         pb = __builtin_amdgcn_readlane(unit_incl[c], 63);
       }
       const int P = pb;

@@ -36,21 +36,57 @@ template <> struct Elem<float> {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Wave64 reductions / scans (ds_swizzle-free: __shfl_* lower to ds_bpermute)
+// Wave64 inclusive scans, every lane active.  Within each row of 16 lanes by data-parallel moves
+// (row_shr 1, 2, 4, 8: lane i adds lane i - s of its row; lanes shifted in from outside the row read
+// 0), then each row adds the totals of the rows below it, read from lanes 15, 31 and 47.  Register
+// moves only, where a shuffle (ds_bpermute) would make six dependent trips through the LDS crossbar.
 // ---------------------------------------------------------------------------------------------
 
-__device__ __forceinline__ long long wave_sum_i64(long long v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+template <int CTRL>
+__device__ __forceinline__ int row_shifted(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += row_shifted<0x111>(v);
+  v += row_shifted<0x112>(v);
+  v += row_shifted<0x114>(v);
+  v += row_shifted<0x118>(v);
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ long long row_shifted_i64(long long v) {
+  const unsigned lo = (unsigned)row_shifted<CTRL>((int)(unsigned)v);
+  const unsigned hi = (unsigned)row_shifted<CTRL>((int)(unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ long long readlane_i64(long long v, int lane) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)((unsigned long long)v >> 32), lane);
+  return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
 __device__ __forceinline__ long long wave_incl_scan_i64(long long v) {
-  const int lane = threadIdx.x & 63;
-  for (int o = 1; o < 64; o <<= 1) {
-    long long n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
-  return v;
+  v += row_shifted_i64<0x111>(v);
+  v += row_shifted_i64<0x112>(v);
+  v += row_shifted_i64<0x114>(v);
+  v += row_shifted_i64<0x118>(v);
+  const long long r0 = readlane_i64(v, 15);
+  const long long r1 = readlane_i64(v, 31);
+  const long long r2 = readlane_i64(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// Sum over the wave, the same in every lane.
+__device__ __forceinline__ long long wave_sum_i64(long long v) {
+  return readlane_i64(wave_incl_scan_i64(v), 63);
 }
 
 // ---------------------------------------------------------------------------------------------

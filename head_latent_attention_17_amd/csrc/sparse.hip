@@ -115,28 +115,12 @@ __global__ __launch_bounds__(256) void index_score_kernel(const int8_t* __restri
   }
 }
 
-// Inclusive scan over the 64 lanes of a wave (every lane active): within each row of 16 lanes by
-// data-parallel moves (row_shr 1, 2, 4, 8; lanes shifted in from outside the row read 0), then
-// each row adds the totals of the rows below it, read from lanes 15, 31 and 47.  Register moves
-// only, where a shuffle would make six round trips through the LDS crossbar.
-__device__ __forceinline__ int wave_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);
-  const int r0 = __builtin_amdgcn_readlane(v, 15);
-  const int r1 = __builtin_amdgcn_readlane(v, 31);
-  const int r2 = __builtin_amdgcn_readlane(v, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
-}
-
 // Inclusive scan over a workgroup of NT threads (one value each) through the wave totals in LDS;
 // the workgroup total goes to *total.
 template <int NT>
 __device__ __forceinline__ int block_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_scan(v);
+  v = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
