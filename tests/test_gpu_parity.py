@@ -140,11 +140,14 @@ def test_out_proj_matches_oracle(lib, f32):
     assert e <= _tol(f32)
 
 
-@pytest.mark.parametrize("heads,batch", [(16, 3), (128, 32), (128, 65), (16, 130), (128, 130)])
+@pytest.mark.parametrize("heads,batch", [(16, 3), (128, 32), (32, 33), (128, 64), (128, 65), (16, 130),
+                                         (128, 130)])
 def test_projections_batch_blocks(lib, heads, batch):
-    """Absorption and out-projection (bf16) against the oracle with 16 and 128 heads: batch 3 and 32
-    (one 32-row block), 65 (three blocks in one pass of the four-block kernel) and 130 (five
-    blocks, two passes, the last with two rows)."""
+    """Absorption and out-projection (bf16) against the oracle with 16, 32 and 128 heads: batch 3 and
+    32 (one 32-row block), 33 and 64 (one 64-row pass of the absorption with two blocks), 65 (the
+    absorption's second pass holds one row; three blocks in one pass of the out-projection's
+    four-block kernel) and 130 (three absorption passes, the last with two rows; five blocks, two
+    passes of the out-projection)."""
     wl = synth.make_custom([3] * batch, heads=heads, seed=62 + batch)
     say("projections", heads, batch)
     g = Gpu(wl)
