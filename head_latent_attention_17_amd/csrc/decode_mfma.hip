@@ -1282,6 +1282,200 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_fp6_kernel(DecodeParams p) 
   wait_vmcnt<0>();
 }
 
+// ---- 16 heads: heads are the 16-wide dimension of v_mfma_f32_16x16x32_bf16 -------------------
+// Each wave computes the scores of the whole tile for all 16 heads (two 16-token blocks x 18
+// k-steps, S^T[t][h] = K . Q^T with the query in 72 VGPRs) and a quarter of the output product (its
+// 128 latent dims: eight 16-dim blocks over the tile's 32 tokens, O^T[d][h] += V^T . P^T), so the
+// query is loaded once per wave and each piece is stored once, where the four-wave 32-column
+// kernel would repeat every head eight times.  The score accumulators give lane l head l % 16 and
+// tokens 4 g .. 4 g + 3 of each block (g = l / 16): its eight probabilities are the B operand of
+// the output product with the tokens in the order {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3}, and
+// the V^T operand reads the same tokens with two transposing reads.  The four waves work out the
+// same softmax (online, base 2, O rescaled whenever a head's maximum rises).  Work units are ranges
+// of 32-token tiles: the plain cut of the batch's tiles over min(units, tiles) units, so every unit
+// holds a tile and small batches spread over more workgroups than they have pages.  Pieces,
+// per-sequence unit table, tile ring and the list mode (TOPK: kept tokens read in place) are those
+// of the kernel above.
+template <bool TOPK>
+__global__ __launch_bounds__(kWaves * 64, 1) void decode_h16_kernel(DecodeParams p) {
+  constexpr int kPer = kBlocks / kWaves;  // copies per wave per tile
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
+  __shared__ __attribute__((aligned(1024))) char ring[kStages][kTileBytes];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long T = total_tiles(p.seq_lens, p.batch);
+  const int W = (int)min((long long)gridDim.x, T);
+  const int w = uni(xcd_unit(blockIdx.x, gridDim.x));
+  if (w >= W) return;
+  TileCursor ld;
+  ld.lens = p.seq_lens;
+  ld.sh = 5;
+  ld.pg0 = uni((int)((long long)w * T / W));
+  ld.pg1 = uni((int)((long long)(w + 1) * T / W));
+  ld.valid = true;
+  ld.all_live = true;
+  {
+    int bb;
+    long long bf;
+    locate_unit(p.seq_lens, p.batch, ld.pg0, 5, bb, bf);
+    ld.b = uni(bb);
+    ld.before = uni((int)bf);
+  }
+  ld.load_seq();
+  ld.enter();
+  TileCursor cp = ld;
+
+  // Per-lane LDS offsets inside a tile (lane = 16 g + j).  Score operand of k-step ks: token
+  // 16 blk + j, latent dims 32 ks + 8 g ..: chunk 4 ks + g, whose odd k-steps flip bit 6 of the
+  // offset and whose chunk group ks / 2 is a whole block.  Output operand of d-block i: dims
+  // 128 wave + 16 i + 4 (j % 4) .. of tokens 4 g + j / 4 (first read) and 16 + 4 g + j / 4 (second
+  // read, 18 blocks on): chunk 16 wave + 2 i + (j % 4) / 2, byte 8 (j % 2); i flips bits 5-6 and
+  // i / 4 is a whole block.
+  const int ln0 = lane_id();
+  const int g = ln0 >> 4, j = ln0 & 15;
+  const unsigned k_base0 = (unsigned)tile_offset(j, g);
+  const unsigned k_base1 = (unsigned)tile_offset(16 + j, g);
+  const unsigned v_base = (unsigned)(tile_offset(4 * g + (j >> 2), 16 * wave + ((j & 3) >> 1)) + 8 * (j & 1));
+  auto lds16 = [](unsigned a) __attribute__((always_inline)) {
+    return *reinterpret_cast<const LDS_AS bf16x8*>((const LDS_AS char*)(uintptr_t)a);
+  };
+  auto lds_tr = [](unsigned a) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)((LDS_AS char*)(uintptr_t)a));
+  };
+
+  const uint16_t* qa = static_cast<const uint16_t*>(p.q_abs);
+  bf16x8 q[18];
+  auto load_q = [&](int b) __attribute__((always_inline)) {
+    const int ln = lane_id();
+    const uint16_t* qrow = qa + ((size_t)b * 16 + (ln & 15)) * kRow + 8 * (ln >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+  };
+  load_q(cp.b);
+
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (ld.valid) {
+      issue_tile<TOPK>(p, ld, (LDS_AS char*)ring[s], wave);
+      ld.advance();
+      ++issued;
+    }
+  }
+  // Loads complete in issue order: with at most the prologue's copies outstanding, Q has landed.
+  if (issued >= 3) wait_vmcnt<3 * kPer>();
+  else if (issued == 2) wait_vmcnt<2 * kPer>();
+  else wait_vmcnt<kPer>();
+  auto tile_ready = [&](int t) __attribute__((always_inline)) {
+    const int younger = issued - t - 1;
+    if (younger >= 2) wait_vmcnt<2 * kPer>();
+    else if (younger == 1) wait_vmcnt<kPer>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+
+  const float scale = p.scale_log2;
+  const unsigned ring0 = (unsigned)(uintptr_t)(LDS_AS char*)ring[0];
+  int it = 0;
+  bool first_segment = true;
+  while (cp.valid) {  // one segment: the part of sequence b inside this unit
+    const int b = cp.b;
+    if (threadIdx.x == 0) {
+      if (cp.t == 0) {
+        p.seq_units[4 * b] = w;
+        p.seq_units[4 * b + 2] = 1;
+      }
+      if (cp.t_end == cp.len) p.seq_units[4 * b + 1] = w;
+    }
+    if (!first_segment) {
+      load_q(b);
+      wait_vmcnt<0>();
+    }
+    first_segment = false;
+    f32x4v o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;  // base-2 running maximum of this lane's head
+    float l_run = 0.f;        // this lane's share of the softmax sum
+    bool last;
+    do {
+      last = cp.last();
+      // The barrier also frees the stage of tile it - 1 for the copies of tile it + 3.
+      tile_ready(it);
+      if (ld.valid) {
+        issue_tile<TOPK>(p, ld, (LDS_AS char*)ring[stage_of(it + kStages - 1)], wave);
+        ld.advance();
+        ++issued;
+      }
+      const unsigned tb = ring0 + (unsigned)stage_of(it) * kTileBytes;
+      f32x4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const unsigned d = 64u * (ks & 1), blk = 1024u * (ks >> 1);
+        const bf16x8 a0 = lds16(((tb + k_base0) ^ d) + blk);
+        const bf16x8 a1 = lds16(((tb + k_base1) ^ d) + blk);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, q[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, q[ks], s1, 0, 0, 0);
+      }
+      // softmax of the tile: tokens past the segment's end (a ragged last tile) take no weight
+      const int n = min(kTileTok, cp.t_end - cp.t);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = 4 * g + i < n ? s0[i] * scale : -INFINITY;
+        v[4 + i] = 16 + 4 * g + i < n ? s1[i] * scale : -INFINITY;
+      }
+      float mx = max3(max3(v[0], v[1], v[2]), max3(v[3], v[4], v[5]), max2(v[6], v[7]));
+      mx = max2(mx, __shfl_xor(mx, 16, 64));
+      mx = max_halves(mx);
+      if (mx > m_run) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mx);  // 0 for the first tile
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] *= alpha;
+        m_run = mx;
+      }
+      bf16x8 pb;
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e = __builtin_amdgcn_exp2f(v[i] - m_run);
+        ls += e;
+        pb[i] = (__bf16)e;
+      }
+      l_run += ls;
+      // output: this wave's eight d-blocks
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned a = ((tb + v_base) ^ (32u * (i & 3))) + 1024u * (i >> 2);
+        const s16x4 v0 = lds_tr(a);
+        const s16x4 v1 = lds_tr(a + 18 * 1024);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[i], 0, 0, 0);
+      }
+      cp.advance();
+      ++it;
+    } while (!last);
+
+    // The piece: this wave's 128 dims of each head, divided by the head's softmax sum, in bf16
+    // (lane 16 g + j: head j, dims 128 wave + 16 i + 4 g .. + 3), with (maximum, sum) per head.
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot = sum_halves(l_tot);
+    const float inv = 1.f / l_tot;
+    const size_t part = ((size_t)w + b) * 16 + j;
+    uint16_t* po = reinterpret_cast<uint16_t*>(p.ws_o + part * kDc) + 128 * wave + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x4 x = {(__bf16)(o[i][0] * inv), (__bf16)(o[i][1] * inv), (__bf16)(o[i][2] * inv),
+                        (__bf16)(o[i][3] * inv)};
+      *reinterpret_cast<u32x2*>(po + 16 * i) = __builtin_bit_cast(u32x2, x);
+    }
+    if (wave == 0 && g == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * part) = make_float2(m_run, l_tot);
+  }
+  // No copy into LDS may still be in flight when the workgroup ends.
+  wait_vmcnt<0>();
+}
+
 }  // namespace
 
 bool mfma_supported(const DecodeParams& p) {
@@ -1299,6 +1493,13 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   if (!mfma_supported(p)) return hipErrorNotSupported;
+  if (p.heads == 16) {
+    if (p.positions)
+      hipLaunchKernelGGL(decode_h16_kernel<true>, dim3(p.num_units), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(decode_h16_kernel<false>, dim3(p.num_units), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   // Every head count runs four waves: below 128 heads their columns repeat heads, which spreads the
   // tile copies over four waves instead of leaving them to H / 32.
   if (p.positions)

@@ -11,12 +11,14 @@
 namespace mla {
 
 int auto_units(int batch, int heads, int max_blocks, bool f32) {
-  // Enough page ranges to give every compute unit work, but never more ranges than pages.  The
-  // matrix-core kernel (bf16) runs one workgroup per compute unit; the fp32 debug kernel splits each
+  // Enough ranges to give every compute unit work, but never more ranges than grains: pages, or
+  // 32-token tiles for the 16-head matrix-core kernel, which cuts tiles.  The
+  // matrix-core kernels (bf16) run one workgroup per compute unit; the fp32 debug kernel splits each
   // range further by 8-head groups, so at 16 heads it takes twice the ranges.
-  const long long pages_bound = (long long)batch * (long long)max_blocks;
+  long long grains_bound = (long long)batch * (long long)max_blocks;
+  if (heads == 16 && !f32) grains_bound *= 2;
   long long units = (f32 && heads < 32) ? 2 * kNumCUs : kNumCUs;
-  if (units > pages_bound) units = pages_bound;
+  if (units > grains_bound) units = grains_bound;
   if (units < 1) units = 1;
   return (int)units;
 }

@@ -89,8 +89,9 @@ int mla_abi_version(void);
  * Bytes of workspace mla_decode needs for these sizes (0 on invalid arguments).
  * num_splits is the number of work units the batch's tokens are cut into (0 = automatic: the value
  * mla_decode would choose): equal page ranges, or with at least 8 tiles of 32 tokens per unit, tile
- * ranges cut so that a unit that starts another sequence holds fewer tiles.  The result does not
- * depend on the sequence lengths.
+ * ranges cut so that a unit that starts another sequence holds fewer tiles.  At 16 heads (bf16) the
+ * units are equal ranges of 32-token tiles, at most one unit per tile.  The result does not depend
+ * on the sequence lengths.
  */
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype);

@@ -49,7 +49,11 @@ def test_workspace_size_formula():
     # one fp32 slot of 512 + 2 values per (piece, head), then 16 bytes per sequence
     assert L.mla_decode_workspace_size(4, 128, 2048, 64) == (64 + 4) * 128 * 514 * 4 + 4 * 16
     assert L.mla_decode_workspace_size(4, 128, 2048, 0) == (256 + 4) * 128 * 514 * 4 + 4 * 16
-    assert L.mla_decode_workspace_size(1, 16, 3, 0) == (3 + 1) * 16 * 514 * 4 + 16   # never more units than pages
+    assert L.mla_decode_workspace_size(1, 32, 3, 0) == (3 + 1) * 32 * 514 * 4 + 16   # never more units than pages
+    assert L.mla_decode_workspace_size(1, 16, 3, 0, 1) == (3 + 1) * 16 * 514 * 4 + 16  # fp32 at 16 heads: pages
+    assert L.mla_decode_workspace_size(1, 16, 3, 0) == (6 + 1) * 16 * 514 * 4 + 16   # 16 heads: 32-token tiles
+    assert L.mla_decode_topk_workspace_size(1, 16, 130) == (6 + 1) * 16 * 514 * 4 + 16
+    assert L.mla_decode_workspace_size(2, 16, 1000, 0) == (256 + 2) * 16 * 514 * 4 + 2 * 16
     assert L.mla_decode_workspace_size(4, 100, 2048, 0) == 0                  # unsupported heads
     assert L.mla_decode_workspace_size(4, 128, 0, 0) == 0
     assert L.mla_decode_workspace_size(4, 128, 8, -1) == 0
