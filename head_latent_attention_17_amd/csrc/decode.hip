@@ -194,6 +194,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int h = blockIdx.y * HPW + threadIdx.x / kTPH;
   const int j = threadIdx.x % kTPH;
   const int len = p.seq_lens[b];
+  const int4 su_entry = seq_units_entry(p, b);
   const long long np = pages_of(len);
   OT* o = static_cast<OT*>(p.o_lat);
   const size_t ob = ((size_t)b * p.heads + h) * kDc;
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     if (p.lse && j == 0) p.lse[(size_t)b * p.heads + h] = -INFINITY;
     return;
   }
-  const SeqUnits su = seq_units_of(p, b, np);
+  const SeqUnits su = seq_units_of(p, b, np, su_entry);
   const int wf = su.wf, wl = su.wl;
   auto live = [&](int w) { return su.live(w); };
   auto slot = [&](int w) { return ((size_t)w + b) * p.heads + h; };
@@ -299,6 +300,7 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(DecodeParams p) {
   const int g = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
   const int len = p.seq_lens[b];
+  const int4 su_entry = seq_units_entry(p, b);
   const long long np = pages_of(len);
   OT* o = static_cast<OT*>(p.o_lat);
   const size_t ob = ((size_t)b * p.heads + h) * kDc;
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(DecodeParams p) {
     }
     return;
   }
-  const SeqUnits su = seq_units_of(p, b, np);
+  const SeqUnits su = seq_units_of(p, b, np, su_entry);
   const int wf = su.wf, wl = su.wl;
   auto live = [&](int w) { return su.live(w); };
   auto slot = [&](int w) { return ((size_t)w + b) * p.heads + h; };

@@ -1366,6 +1366,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_h16_kernel(DecodeParams
   if (issued >= 3) wait_vmcnt<3 * kPer>();
   else if (issued == 2) wait_vmcnt<2 * kPer>();
   else wait_vmcnt<kPer>();
+  // The copies are invisible to the compiler, so it cannot tell that this wait covered the query: it
+  // would wait for its loads again inside the tile loop, before every score MFMA of every tile (and,
+  // counting the copies too, drain the ring each time).  Using Q here puts those waits here, once.
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) asm volatile("" : : "v"(q[ks]));
   auto tile_ready = [&](int t) __attribute__((always_inline)) {
     const int younger = issued - t - 1;
     if (younger >= 2) wait_vmcnt<2 * kPer>();
@@ -1400,7 +1405,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_h16_kernel(DecodeParams
     bool last;
     do {
       last = cp.last();
-      // The barrier also frees the stage of tile it - 1 for the copies of tile it + 3.
+      // The barrier also frees the stage of tile it - 1 for the copies of tile it + 3.  (Spread one
+      // per two score k-steps, as in the kernel above, they measured slower here: 161-165 against
+      // 148 us at 4 x 131,072 tokens.)
       tile_ready(it);
       if (ld.valid) {
         issue_tile<TOPK>(p, ld, (LDS_AS char*)ring[stage_of(it + kStages - 1)], wave);

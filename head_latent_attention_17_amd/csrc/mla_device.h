@@ -337,12 +337,17 @@ struct SeqUnits {
   }
 };
 
-__device__ __forceinline__ SeqUnits seq_units_of(const DecodeParams& p, int b, long long np) {
+// The table's entry of sequence b, read together with its length (one memory round trip instead of
+// two; the entry of an empty sequence is never written and never used).
+__device__ __forceinline__ int4 seq_units_entry(const DecodeParams& p, int b) {
+  return p.seq_units ? *reinterpret_cast<const int4*>(p.seq_units + 4 * b) : make_int4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ SeqUnits seq_units_of(const DecodeParams& p, int b, long long np, int4 d) {
   SeqUnits u;
   u.W = p.num_units;
   u.P = 0;
   if (p.seq_units) {
-    const int4 d = *reinterpret_cast<const int4*>(p.seq_units + 4 * b);
     u.wf = d.x;
     u.wl = d.y;
     u.all_live = d.z != 0;
