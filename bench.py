@@ -316,8 +316,9 @@ def sparse_timing(lib, synth, wl, dev, q_abs, bt, att, cache, steps: int, dense_
 def measured_peaks(dev, lib=None):
     """What this GPU reaches on plain work, as the second reference the roofline fractions are quoted
     against: a 2 GiB device copy (bytes read + written; torch's float32 sum over the same array reads
-    at only about 4 TB/s, so it is no measure of the peak), an 8,192-cube bf16 matrix product (torch /
-    hipBLASLt), and the matrix-core rate itself (mla_calibrate_mfma: every SIMD issuing independent
+    at only about 4 TB/s, so it is no measure of the peak), plain reads moved the way the decode moves
+    its tiles (mla_calibrate_read), an 8,192-cube bf16 matrix product (torch / hipBLASLt), and the
+    matrix-core rate itself (mla_calibrate_mfma: every SIMD issuing independent
     v_mfma_f32_32x32x16_bf16 back to back, the decode's instruction).  Each timed with HIP events,
     best of five after two untimed runs."""
     import torch
@@ -356,6 +357,15 @@ def measured_peaks(dev, lib=None):
         out["mfma_issue_bf16_tflops"] = round(blocks * 4 * iters * 4 * 32 * 32 * 16 * 2 / t / 1e12, 1)
         out["how"] += ("; mla_calibrate_mfma: 1,024 workgroups x 4 waves x 16,384 independent "
                        "v_mfma_f32_32x32x16_bf16 each")
+        # plain reads moved like the decode's tiles: 2.25 GiB, HBM -> LDS in 36 KB chunks
+        src = torch.empty(65536 * 36 * 1024, dtype=torch.uint8, device=dev)
+        res = torch.empty(512, dtype=torch.int32, device=dev)
+        t = best(lambda: lib.mla_calibrate_read(src, res, 512))
+        out["hbm_read_gbs"] = round(src.numel() / t / 1e9, 1)
+        out["how"] += ("; mla_calibrate_read: 2.25 GiB read HBM -> LDS in 36,864-byte chunks by 512 "
+                       "workgroups, three chunks in flight each")
+        del src
+        torch.cuda.empty_cache()
     return out
 
 
@@ -428,7 +438,10 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str):
             raise SystemExit(f"{counter}: no calibration copy found in {folder}")
         scale = CALIB_BYTES / calib
         total = 0.0
-        for tag in ("decode_mfma_kernel", "merge"):
+        # the decode kernel (the 16-head one at 16 heads; never the ~6-bit one), then the merge
+        tags = ("decode_h16_kernel",) if any("decode_h16_kernel" in r["Kernel_Name"] for r in rows) \
+            else ("decode_mfma_kernel",)
+        for tag in tags + ("merge",):
             vals = [float(r["Counter_Value"]) * 1024 for r in rows
                     if tag in r["Kernel_Name"] and "out_proj" not in r["Kernel_Name"]]
             if not vals:
@@ -810,6 +823,7 @@ def main():
         "roofline": dict(dc, kernel="mla_decode (decode + merge kernels, one call per layer)",
                          measured_peaks=peaks,
                          frac_of_measured_copy=round(dc["achieved"] / peaks["hbm_copy_gbs"], 4),
+                         frac_of_measured_read=round(dc["achieved"] / peaks["hbm_read_gbs"], 4),
                          mfma_frac_of_measured=round(dc["mfma_tflops"] / peaks["mfma_bf16_tflops"], 4),
                          mfma_frac_of_issue_rate=round(dc["mfma_tflops"] / peaks["mfma_issue_bf16_tflops"], 4)),
         "calls_per_layer": main_rec["calls_per_layer"],

@@ -16,5 +16,5 @@ from ._lib import (FP6_PAGE_BYTES, INDEX_DIM, MLA_BF16, MLA_F32, MLAError, mla_a
                    mla_out_proj_hidden_workspace_size, mla_index_topk, mla_index_topk_workspace_size,
                    mla_gather_rows, mla_decode_topk, mla_decode_topk_workspace_size, mla_status_string,
                    mla_decode_noalloc, mla_decode_noalloc_max_bytes, mla_decode_out_proj,
-                   mla_decode_out_proj_workspace_size, mla_calibrate_mfma,
+                   mla_decode_out_proj_workspace_size, mla_calibrate_mfma, mla_calibrate_read,
                    LIB_PATH)

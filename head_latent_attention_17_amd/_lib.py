@@ -22,7 +22,7 @@ EXPORTS = ("mla_status_string", "mla_abi_version", "mla_decode_workspace_size", 
            "mla_absorb_q", "mla_decode", "mla_out_proj", "mla_cache_append_hidden_workspace_size",
            "mla_cache_append_hidden", "mla_cache_append_fp6", "mla_cache_quantize_fp6", "mla_decode_fp6",
            "mla_out_proj_hidden_workspace_size", "mla_out_proj_hidden", "mla_index_topk_workspace_size",
-           "mla_index_topk", "mla_gather_rows", "mla_decode_topk_workspace_size", "mla_decode_topk", "mla_decode_noalloc_max_bytes", "mla_calibrate_mfma",
+           "mla_index_topk", "mla_gather_rows", "mla_decode_topk_workspace_size", "mla_decode_topk", "mla_decode_noalloc_max_bytes", "mla_calibrate_mfma", "mla_calibrate_read",
            "mla_decode_noalloc", "mla_decode_out_proj_workspace_size", "mla_decode_out_proj")
 INDEX_DIM = 128          # MLA_INDEX_DIM: int8 numbers in a token's index vector
 FP6_PAGE_BYTES = 27904   # MLA_FP6_PAGE_BYTES: 64 rows of 432 code bytes, then 64 float32 scales
@@ -47,6 +47,8 @@ lib.mla_decode.restype = _i
 lib.mla_decode.argtypes = [_p, _p, _i, _i, _p, _i, _p, _i, _i, _f, _p, _p, _p, _sz, _i, _i, _p]
 lib.mla_calibrate_mfma.restype = _i
 lib.mla_calibrate_mfma.argtypes = [_p, _i, _i, _p]
+lib.mla_calibrate_read.restype = _i
+lib.mla_calibrate_read.argtypes = [_p, ctypes.c_size_t, _p, _i, _p]
 lib.mla_decode_noalloc_max_bytes.restype = _sz
 lib.mla_decode_noalloc_max_bytes.argtypes = []
 lib.mla_decode_noalloc.restype = _i
@@ -222,6 +224,17 @@ def mla_calibrate_mfma(out, blocks: int, iters: int, stream=None):
     if out.dtype != torch.float32 or out.numel() < 4 * blocks:
         raise ValueError("out must be a float32 tensor of at least blocks * 4 elements")
     _check(lib.mla_calibrate_mfma(_ptr(out), int(blocks), int(iters), _stream(stream)), "mla_calibrate_mfma")
+
+
+def mla_calibrate_read(buf, out, blocks: int, stream=None):
+    """buf: device tensor whose byte size is a multiple of 36,864; out: int32 device tensor of at
+    least `blocks` elements; see the header for the rate."""
+    _dev(buf)
+    _dev(out)
+    if out.dtype != torch.int32 or out.numel() < blocks:
+        raise ValueError("out must be an int32 tensor of at least `blocks` elements")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.mla_calibrate_read(_ptr(buf), nbytes, _ptr(out), int(blocks), _stream(stream)), "mla_calibrate_read")
 
 
 def mla_decode_noalloc_max_bytes() -> int:

@@ -63,7 +63,7 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_abi_version(void) { return 107; }
+int mla_abi_version(void) { return 108; }
 
 size_t mla_decode_workspace_size(int batch, int num_heads, int max_blocks_per_seq, int num_splits,
                                  mla_dtype dtype) {
@@ -283,6 +283,12 @@ mla_status mla_calibrate_mfma(float* out, int blocks, int iters, hipStream_t str
   if (!out) return MLA_ERR_NULL;
   if (blocks < 1 || iters < 1) return MLA_ERR_SHAPE;
   return launch_mfma_rate(out, blocks, iters, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_calibrate_read(const void* buf, size_t bytes, int* out, int blocks, hipStream_t stream) {
+  if (!buf || !out) return MLA_ERR_NULL;
+  if (blocks < 1 || bytes == 0 || bytes % (36 * 1024) != 0) return MLA_ERR_SHAPE;
+  return launch_read_rate(buf, bytes, out, blocks, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 mla_status mla_decode_noalloc(const void* q_abs, const void* kv_cache, int num_pages, int page_size,

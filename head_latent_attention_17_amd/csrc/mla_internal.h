@@ -107,6 +107,7 @@ hipError_t check_tables(const int32_t* block_table, int max_blocks, const int32_
 // Matrix-core rate kernel: `blocks` workgroups of four waves, each wave `iters` x 4 independent
 // v_mfma_f32_32x32x16_bf16; out holds one float per wave (blocks * 4).
 hipError_t launch_mfma_rate(float* out, int blocks, int iters, hipStream_t s);
+hipError_t launch_read_rate(const void* buf, size_t bytes, int* out, int blocks, hipStream_t s);
 // Device address of this device's fixed scratch array (kNoAllocScratchBytes), looked up on the first
 // call on each device; allocates nothing.
 hipError_t noalloc_scratch(void** out);

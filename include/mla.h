@@ -329,6 +329,18 @@ mla_status mla_decode_topk(const void* q_abs, const void* kv_cache, int num_page
  */
 mla_status mla_calibrate_mfma(float* out, int blocks, int iters, hipStream_t stream);
 
+/*
+ * Read-rate calibration (for reading the decode's roofline; not part of the decode path).
+ * Launches `blocks` workgroups of four waves on `stream` that read buf (device, `bytes` of it, a
+ * positive multiple of 36,864, not written) in 36,864-byte chunks, chunk c by workgroup c mod blocks,
+ * HBM -> LDS with the 16-byte LDS-direct loads the decode uses for its tiles, three chunks in flight
+ * per workgroup.  out[g] (int, device, `blocks` of them, written) is the XOR of the first 32-bit word
+ * of every chunk workgroup g read.  The caller times the launch: rate = bytes / duration.
+ * Errors: MLA_ERR_NULL (buf or out), MLA_ERR_SHAPE (blocks < 1, bytes 0 or not a multiple of
+ * 36,864), MLA_ERR_HIP.
+ */
+mla_status mla_calibrate_read(const void* buf, size_t bytes, int* out, int blocks, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

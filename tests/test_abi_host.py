@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.mla_abi_version() == 107
+    assert L.mla_abi_version() == 108
     for code, name in L.STATUS.items():
         assert L.mla_status_string(code).startswith(name)
     assert "unknown" in L.mla_status_string(12345)
@@ -311,3 +311,15 @@ def test_decode_out_proj_validation_and_workspace():
     assert call(dtype=5) == -3
     assert call(batch=-2) == -2
     assert call(batch=0) == 0
+
+
+def test_calibrate_read_validation():
+    """The read-rate calibration validates before launching: null pointers, block counts and sizes
+    that are not whole 36,864-byte chunks are rejected without touching the GPU."""
+    L = _lib()
+    f = L.lib.mla_calibrate_read
+    assert f(None, 36864, FAKE, 1, None) == -1
+    assert f(FAKE, 36864, None, 1, None) == -1
+    assert f(FAKE, 36864, FAKE, 0, None) == -2
+    assert f(FAKE, 0, FAKE, 1, None) == -2
+    assert f(FAKE, 36864 + 4, FAKE, 1, None) == -2
