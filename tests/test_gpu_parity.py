@@ -74,6 +74,44 @@ def test_split_count_invariance(lib, splits):
     assert lse_err(g.lse.cpu().numpy()[:, hs], lse_ref[:, hs]) <= BF16_TOL
 
 
+@pytest.mark.parametrize("splits", [1, 5, 0, 300])
+def test_sixteen_heads_tile_cut(lib, splits):
+    """The 16-head kernel cuts the batch's 32-token tiles over min(units, tiles) units: 70 sequences
+    (more than one 64-sequence pass over the lengths), every 9th empty, ragged lengths, with one
+    unit, a few, the automatic count and more units than tiles.  Sampled sequences against the
+    oracle on all 16 heads, the empty ones exactly zero with lse -inf, and the result of every cut
+    within rounding of the one-unit cut."""
+    rng = np.random.default_rng(316)
+    lens = [int(x) for x in rng.integers(1, 200, 70)]
+    for i in range(0, len(lens), 9):
+        lens[i] = 0
+    lens[5] = 1
+    lens[6] = 32
+    lens[7] = 33
+    wl = synth.make_custom(lens, heads=16, seed=316)
+    tiles = sum((n + 31) // 32 for n in lens)
+    assert splits < tiles or splits == 300 and splits > tiles
+    say("16 heads, tile cut", wl.batch, "tiles", tiles, "splits", splits)
+    g = Gpu(wl)
+    g.step(lib, splits=splits, q_abs_from_absorb=False)
+    torch.cuda.synchronize()
+    sel = [b for b in sorted(set(range(1, wl.batch, 4)) | {5, 6, 7, wl.batch - 1}) if lens[b] > 0]
+    hi = host_inputs(wl, 0, sel)
+    o_ref, lse_ref = O.latent_decode_batch(hi["q_lat"], hi["cache"], wl.block_table, wl.attended_lens,
+                                           wl.scale, batch=sel)
+    o = to_host_f64(g.o_lat)
+    e = rel_err(o[sel], o_ref[sel])
+    e_l = lse_err(g.lse.cpu().numpy()[sel], lse_ref[sel])
+    say(f"  err {e:.3e}  lse err {e_l:.3e}")
+    assert e <= BF16_TOL and e_l <= BF16_TOL
+    empty = [b for b in range(wl.batch) if lens[b] == 0]
+    assert np.all(o[empty] == 0) and torch.all(torch.isneginf(g.lse[empty]))
+    g1 = Gpu(wl)
+    g1.step(lib, splits=1, q_abs_from_absorb=False)
+    torch.cuda.synchronize()
+    assert rel_err(to_host_f64(g.o_lat)[sel], to_host_f64(g1.o_lat)[sel]) <= BF16_TOL
+
+
 @pytest.mark.parametrize("splits", [0, 97])
 def test_many_sequences_cost_weighted_cut(lib, splits):
     """300 sequences of mixed lengths, every 23rd empty, with at least 8 tiles per unit: the units
