@@ -7,8 +7,9 @@
 // All heads of a sequence share every cached row (the row is per token, not per head), so heads
 // form the N dimension of both products and each row is read from HBM once per launch.
 //
-// Workgroup = 4 waves x 32 heads = 128 heads, one workgroup per compute unit (fewer heads: the
-// waves' columns repeat heads, see head_of).  Per 32-token tile:
+// Workgroup = 4 waves x 32 heads = 128 heads, one workgroup per compute unit (64 and 32 heads: the
+// waves' columns repeat heads, see head_of; 16 heads run decode_h16_kernel, below, on the 16-wide
+// matrix instruction).  Per 32-token tile:
 //   scores  S^T[t][h] = K . Q^T   M = 32 tokens, N = 32 heads, K = 576  (36 MFMAs per wave)
 //   output  O^T[d][h] = V^T . P^T M = 32 dims,   N = 32 heads, K = 32   (16 blocks x 2 MFMAs)
 // Q stays in VGPRs for a whole segment; O^T (32 x 512 fp32 per wave) stays in the 256 AGPRs.  The
@@ -35,7 +36,8 @@
 // transposing read (4 tokens x 2 chunks) always land on 16 different 16-byte bank groups.
 //
 // The file also holds the decode over the ~6-bit cache (decode_fp6_kernel, below): the same work
-// split, ring and softmax, with operands converted from the codes in registers.
+// split, ring and softmax, with operands converted from the codes in registers; and the 16-head
+// decode (decode_h16_kernel, at the end).
 #include "mla_device.h"
 
 namespace mla {
