@@ -1305,25 +1305,43 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_h16_kernel(DecodeParams
   __shared__ __attribute__((aligned(1024))) char ring[kStages][kTileBytes];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const long long T = total_tiles(p.seq_lens, p.batch);
-  const int W = (int)min((long long)gridDim.x, T);
   const int w = uni(xcd_unit(blockIdx.x, gridDim.x));
-  if (w >= W) return;
   TileCursor ld;
   ld.lens = p.seq_lens;
   ld.sh = 5;
-  ld.pg0 = uni((int)((long long)w * T / W));
-  ld.pg1 = uni((int)((long long)(w + 1) * T / W));
   ld.valid = true;
   ld.all_live = true;
-  {
+  if (p.batch <= 64) {
+    // One read of the lengths (lane b holds sequence b's) gives the tile count, the unit's first
+    // sequence and that sequence's length: no second pass and no scalar reload of the length.
+    const int lane = threadIdx.x & 63;
+    const int len_l = lane < p.batch ? max(p.seq_lens[lane], 0) : 0;
+    const long long nt = tiles_of(len_l);
+    const long long incl = wave_incl_scan_i64(nt);
+    const long long T = readlane_i64(incl, 63);
+    const int W = (int)min((long long)gridDim.x, T);
+    if (w >= W) return;
+    ld.pg0 = uni((int)((long long)w * T / W));
+    ld.pg1 = uni((int)((long long)(w + 1) * T / W));
+    const unsigned long long hit = __ballot(lane < p.batch && incl > ld.pg0);
+    const int first = __ffsll((long long)hit) - 1;
+    ld.b = uni(first);
+    ld.before = uni((int)readlane_i64(incl - nt, first));
+    ld.len = __builtin_amdgcn_readlane(len_l, first);
+    ld.np = tiles_of(ld.len);
+  } else {
+    const long long T = total_tiles(p.seq_lens, p.batch);
+    const int W = (int)min((long long)gridDim.x, T);
+    if (w >= W) return;
+    ld.pg0 = uni((int)((long long)w * T / W));
+    ld.pg1 = uni((int)((long long)(w + 1) * T / W));
     int bb;
     long long bf;
     locate_unit(p.seq_lens, p.batch, ld.pg0, 5, bb, bf);
     ld.b = uni(bb);
     ld.before = uni((int)bf);
+    ld.load_seq();
   }
-  ld.load_seq();
   ld.enter();
   TileCursor cp = ld;
 
